@@ -1,0 +1,231 @@
+/* moe_mi355x.h -- C ABI of the MI355X (gfx950) mixture-of-experts FFN forward.
+ *
+ * The layer: router top-K over caller-supplied logits, expert-contiguous
+ * permutation of the (token, slot) pairs, a grouped gate||up GEMM with the
+ * gated activation fused into its epilogue, a grouped down GEMM, and a
+ * deterministic router-weighted combine.  Expert weights are dense f32, dense
+ * bf16, or MXFP4 (weight-only: e2m1 codes with e8m0 block scales, decoded
+ * inside the GEMM; the activation stays bf16).
+ *
+ * The calls mirror the lifecycle on the clika "ClikaRT::nn::QMoEWoQ" page
+ * (make -> set_weights -> optional initialize -> forward) and the Python
+ * "MoE" page (constructor geometry and options, set_weights slot names,
+ * forward(x, router_logits, shared_output)).  Option semantics follow the
+ * logicaffeine "MoeSpec" fields and the graiphic ONNX "MoE" attributes.
+ *
+ * Conventions for every call:
+ *  - Tensors are described by moe_tensor: a DEVICE pointer to row-major,
+ *    contiguous data plus its logical dtype and shape.  The library never
+ *    copies, frees or retains caller memory beyond what each call states.
+ *  - Every function returns a moe_status; on failure nothing was launched and
+ *    moe_last_error() holds a message for the calling thread.  No C++
+ *    exception crosses this boundary.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    stream-ordered and never synchronise the host.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1, /* null handle/pointer, bad option value          */
+    MOE_ERR_SHAPE_MISMATCH = 2,   /* a tensor's dtype or shape differs from the
+                                     declaration (QMoEWoQ set_weights / forward)    */
+    MOE_ERR_NOT_DECLARED = 3,     /* a bias bound to a slot make() did not declare
+                                     (QMoEWoQ set_weights)                          */
+    MOE_ERR_UNBOUND = 4,          /* forward/prepare before set_weights
+                                     (QMoEWoQ initialize, "still-fake slot")        */
+    MOE_ERR_UNSUPPORTED = 5,      /* a valid request this build does not serve,
+                                     e.g. a dtype cast of quantised experts
+                                     (QMoEWoQ to_impl(DataType))                    */
+    MOE_ERR_WORKSPACE = 6,        /* workspace missing, too small or misaligned     */
+    MOE_ERR_HIP = 7               /* the HIP runtime reported an error              */
+} moe_status;
+
+typedef enum moe_dtype {
+    MOE_DTYPE_F32 = 0,
+    MOE_DTYPE_BF16 = 1,
+    MOE_DTYPE_MXFP4 = 2,  /* weights only: codes uint8 [..., K/2] (element 2i in the
+                             low nibble of byte i) + e8m0 scales uint8 [..., K/32]   */
+    MOE_DTYPE_I32 = 3
+} moe_dtype;
+
+/* MoeSpec `score`: softmax over every logit, or each logit's own sigmoid. */
+typedef enum moe_scoring { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 } moe_scoring;
+
+/* Gated activation: SiLU-gated h = silu(g)*u, or the clamped SwiGLU
+ * h = g'*sigmoid(alpha*g')*(u'+beta), g' = min(g,L), u' = clamp(u,-L,L),
+ * L = swiglu_limit (L <= 0: no clamp) -- ONNX MoE activation_alpha/beta and
+ * swiglu_limit; clika MoE options swiglu_alpha/beta/limit. */
+typedef enum moe_activation {
+    MOE_ACT_SILU_GATED = 0,
+    MOE_ACT_SWIGLU_CLAMPED = 1
+} moe_activation;
+
+/* ONNX MoE `swiglu_fusion`: 0 not fused (separate gate and up stacks),
+ * 1 fused interleaved (row 2i gate, 2i+1 up), 2 fused not interleaved
+ * (rows [0,I) gate, [I,2I) up). */
+typedef enum moe_swiglu_fusion {
+    MOE_FUSION_NONE = 0,
+    MOE_FUSION_INTERLEAVED = 1,
+    MOE_FUSION_SPLIT = 2
+} moe_swiglu_fusion;
+
+/* Routing and activation options (QMoEWoQ MoeOptions; clika MoE **options). */
+typedef struct moe_options {
+    int32_t scoring;              /* moe_scoring; default SOFTMAX                   */
+    int32_t renormalize;          /* MoeSpec `renormalize`; default 0 (ONNX
+                                     normalize_routing_weights default False).
+                                     The renormalising sum is clamped at 2^-14
+                                     (MoeSpec `sum_can_clamp`).                    */
+    int32_t n_group;              /* group limit (MoeSpec/Moe `groups`): 0 = off;
+                                     else E % n_group == 0, n_group <= 64          */
+    int32_t topk_group;           /* groups kept, 1..n_group                         */
+    float routed_scaling_factor;  /* MoeSpec `scale`, applied after renormalisation;
+                                     default 1                                      */
+    int32_t activation;           /* moe_activation; default SILU_GATED              */
+    int32_t swiglu_fusion;        /* moe_swiglu_fusion; default SPLIT                */
+    float swiglu_alpha;           /* default 1                                       */
+    float swiglu_beta;            /* default 0                                       */
+    float swiglu_limit;           /* default 0 = no clamp                            */
+    int32_t gemm_variant;         /* grouped-GEMM tiles: 0 auto (by rows per expert),
+                                     1 large-M (prefill) tiles, 2 small-M (decode)
+                                     tiles; f32 layers ignore it.  Default 0       */
+} moe_options;
+
+/* A device tensor view.  ndim == 0 (or data == NULL) marks an absent tensor.
+ * For MXFP4 the logical shape counts elements ([E, N, K]); `data` holds the
+ * packed codes and `scales` the e8m0 bytes. */
+typedef struct moe_tensor {
+    const void *data;
+    const uint8_t *scales;        /* MXFP4 only; NULL otherwise                     */
+    int32_t dtype;                /* moe_dtype                                       */
+    int32_t ndim;
+    int64_t shape[4];
+} moe_tensor;
+
+/* Weight slots, named as clika MoE.set_weights / QMoEWoQ::set_weights.
+ *  gate_up_experts : fused [E, 2I, H] (layout per swiglu_fusion);
+ *                    not fused: the UP rows [E, I, H]
+ *  gate_experts    : not fused only: the GATE rows [E, I, H]
+ *  down_experts    : [E, H, I]
+ *  gate_up_bias    : fused [E, 2I]; not fused: up bias [E, I]   (x dtype)
+ *  gate_bias       : not fused only: gate bias [E, I]           (x dtype)
+ *  down_bias       : [E, H]                                     (x dtype)
+ *  e_score_correction_bias : [E] f32 selection bias; binds even when no bias
+ *                    was declared (clika MoE.set_weights).  It is added to the
+ *                    score for SELECTION only; weights use the score alone
+ *                    (MoeSpec `selection_bias`). */
+typedef struct moe_weights {
+    moe_tensor gate_up_experts;
+    moe_tensor down_experts;
+    moe_tensor gate_experts;
+    moe_tensor gate_up_bias;
+    moe_tensor down_bias;
+    moe_tensor gate_bias;
+    moe_tensor e_score_correction_bias;
+} moe_weights;
+
+/* Optional copies of the routing state of a forward (all DEVICE pointers,
+ * each may be NULL).  Sizes: topk_ids, topk_weights [T, K]; expert_counts [E];
+ * expert_offsets [E+1]; row_token, slot_row [T*K].  Rows of the permutation
+ * are grouped by expert, ascending token order within an expert:
+ * row_token[r] is the token of row r and slot_row[t*K+j] the row of (t, j). */
+typedef struct moe_routing_out {
+    int32_t *topk_ids;
+    float *topk_weights;
+    int32_t *expert_counts;
+    int32_t *expert_offsets;
+    int32_t *row_token;
+    int32_t *slot_row;
+} moe_routing_out;
+
+typedef struct moe_layer moe_layer;
+
+/* Fill `opts` with the defaults listed in moe_options. */
+moe_status moe_options_default(moe_options *opts);
+
+/* Declare a layer (QMoEWoQ::make / clika MoE.__init__): geometry E, H, I,
+ * top_k (1 <= top_k <= min(E, 64)), the expert weight dtype (F32, BF16 or
+ * MXFP4), which bias slots exist, and the options (NULL = defaults).
+ * Validation: E <= 1024; with a group limit, E % n_group == 0 and
+ * top_k <= topk_group * E / n_group; MXFP4 needs H and I multiples of 32;
+ * dense weights need H and I multiples of 8.  The handle owns no device
+ * memory.  Errors: INVALID_ARGUMENT. */
+moe_status moe_create(int64_t num_experts, int64_t hidden_size,
+                      int64_t intermediate_size, int64_t top_k,
+                      moe_dtype weight_dtype, int has_gate_up_bias,
+                      int has_down_bias, const moe_options *opts,
+                      moe_layer **out_layer);
+
+/* Bind the weight slots (QMoEWoQ::set_weights).  The library BORROWS the
+ * device buffers: the caller keeps them alive and unchanged until the next
+ * set_weights or moe_destroy.  Re-binding replaces the previous binding.
+ * Errors: SHAPE_MISMATCH (dtype/geometry differs from the declaration, or a
+ * required stack is missing), NOT_DECLARED (a gate/up/down bias given
+ * without its declared slot). */
+moe_status moe_set_weights(moe_layer *layer, const moe_weights *w);
+
+/* Optional warm-up (QMoEWoQ::initialize): checks that every declared slot is
+ * bound.  Idempotent.  Errors: UNBOUND. */
+moe_status moe_prepare(moe_layer *layer, void *stream);
+
+/* Device workspace bytes a forward (or moe_route) on T tokens needs.  The
+ * caller allocates it (256-byte aligned) and may reuse it across calls that
+ * do not overlap in time. */
+moe_status moe_workspace_size(const moe_layer *layer, int64_t T, size_t *bytes);
+
+/* One MoE step (QMoEWoQ::forward): x [T, H] (or [B, S, H]) and the
+ * caller-computed router_logits [T, E] f32 -> out with x's shape and dtype.
+ * x dtype: F32 for F32 weights, BF16 for BF16 or MXFP4 weights.  Optional
+ * shared_output (the shared-expert branch, EXACTLY x's shape and dtype) is
+ * added inside the combine.  `routing` (nullable) receives copies of the
+ * routing state.  T = 0 launches nothing.
+ * Errors: INVALID_ARGUMENT, SHAPE_MISMATCH, UNBOUND, UNSUPPORTED, WORKSPACE,
+ * HIP.  Concurrent calls on one layer are allowed with distinct workspaces. */
+moe_status moe_forward(const moe_layer *layer, const moe_tensor *x,
+                       const moe_tensor *router_logits,
+                       const moe_tensor *shared_output, moe_tensor *out,
+                       void *workspace, size_t workspace_bytes,
+                       moe_routing_out *routing, void *stream);
+
+/* moe_forward with stage timing, for profilers and benchmarks: `events`
+ * holds MOE_STAGE_EVENTS hipEvent_t handles created by the caller; they are
+ * recorded on `stream` before routing, after routing, after the permutation,
+ * after the gate||up GEMM, after the down GEMM and after the combine.  Any
+ * entry may be NULL.  Same errors as moe_forward. */
+#define MOE_STAGE_EVENTS 6
+moe_status moe_forward_timed(const moe_layer *layer, const moe_tensor *x,
+                             const moe_tensor *router_logits,
+                             const moe_tensor *shared_output, moe_tensor *out,
+                             void *workspace, size_t workspace_bytes,
+                             moe_routing_out *routing, void *stream,
+                             void *const *events);
+
+/* Routing and permutation alone (the first two steps of moe_forward):
+ * router_logits [T, E] f32 -> `routing` (non-NULL; any member may be NULL).
+ * Needs moe_workspace_size(T) bytes of workspace. */
+moe_status moe_route(const moe_layer *layer, const moe_tensor *router_logits,
+                     moe_routing_out *routing, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Release the handle (~QMoEWoQ).  Never frees caller buffers.  NULL is a no-op. */
+moe_status moe_destroy(moe_layer *layer);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char *moe_last_error(void);
+
+/* Static name of a status code. */
+const char *moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

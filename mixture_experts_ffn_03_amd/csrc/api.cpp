@@ -1,0 +1,629 @@
+// C-ABI host runtime of the MI355X MoE FFN forward: argument validation,
+// workspace carving, kernel selection and launches on the caller's stream.
+// Lifecycle and error semantics follow the clika "ClikaRT::nn::QMoEWoQ" page
+// (make, set_weights, initialize, forward, to) and the Python "MoE" page
+// (constructor, set_weights slot names, forward signature).
+#include "../../include/moe_mi355x.h"
+#include "moe_kernels.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+using namespace moe;
+
+struct moe_layer {
+    int64_t E, H, I, K;
+    moe_dtype wdtype;
+    int has_gu_bias, has_d_bias;
+    moe_options opts;
+    moe_weights w;
+    bool bound;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+bool present(const moe_tensor &t)
+{
+    return t.data != nullptr && t.ndim > 0;
+}
+
+const char *dtype_name(int d)
+{
+    switch (d) {
+    case MOE_DTYPE_F32: return "f32";
+    case MOE_DTYPE_BF16: return "bf16";
+    case MOE_DTYPE_MXFP4: return "mxfp4";
+    case MOE_DTYPE_I32: return "i32";
+    default: return "?";
+    }
+}
+
+// Check dtype and exact shape of a bound tensor.
+moe_status check_tensor(const char *name, const moe_tensor &t, int dtype,
+                        std::initializer_list<int64_t> shape)
+{
+    if (t.dtype != dtype)
+        return fail(MOE_ERR_SHAPE_MISMATCH, "%s: dtype %s, expected %s", name,
+                    dtype_name(t.dtype), dtype_name(dtype));
+    if (t.ndim != (int)shape.size())
+        return fail(MOE_ERR_SHAPE_MISMATCH, "%s: %d dims, expected %d", name, t.ndim,
+                    (int)shape.size());
+    int i = 0;
+    for (int64_t d : shape) {
+        if (t.shape[i] != d)
+            return fail(MOE_ERR_SHAPE_MISMATCH, "%s: dim %d is %lld, expected %lld", name, i,
+                        (long long)t.shape[i], (long long)d);
+        ++i;
+    }
+    if (dtype == MOE_DTYPE_MXFP4 && t.scales == nullptr)
+        return fail(MOE_ERR_SHAPE_MISMATCH, "%s: MXFP4 stack without scales", name);
+    return MOE_OK;
+}
+
+int act_dtype(const moe_layer *l)
+{
+    return l->wdtype == MOE_DTYPE_F32 ? MOE_DTYPE_F32 : MOE_DTYPE_BF16;
+}
+
+bool fused(const moe_layer *l)
+{
+    return l->opts.swiglu_fusion != MOE_FUSION_NONE;
+}
+
+moe_status check_bound(const moe_layer *l)
+{
+    if (!l->bound) return fail(MOE_ERR_UNBOUND, "weights not bound (call moe_set_weights)");
+    if (!present(l->w.gate_up_experts) || !present(l->w.down_experts))
+        return fail(MOE_ERR_UNBOUND, "gate_up_experts / down_experts slot unbound");
+    if (!fused(l) && !present(l->w.gate_experts))
+        return fail(MOE_ERR_UNBOUND, "gate_experts slot unbound (swiglu_fusion = NONE)");
+    if (l->has_gu_bias) {
+        if (!present(l->w.gate_up_bias))
+            return fail(MOE_ERR_UNBOUND, "declared gate_up_bias slot unbound");
+        if (!fused(l) && !present(l->w.gate_bias))
+            return fail(MOE_ERR_UNBOUND, "declared gate_bias slot unbound");
+    }
+    if (l->has_d_bias && !present(l->w.down_bias))
+        return fail(MOE_ERR_UNBOUND, "declared down_bias slot unbound");
+    return MOE_OK;
+}
+
+size_t align256(size_t v)
+{
+    return (v + 255) & ~(size_t)255;
+}
+
+// Workspace carving.  Every region starts on a 256-byte boundary.
+struct Workspace {
+    size_t ids, weights, block_counts, block_base, counts, offsets, tile_cum1, tile_cum2,
+        row_token, slot_row, h, y, total;
+};
+
+Workspace layout(const moe_layer *l, int64_t T)
+{
+    Workspace w{};
+    const int64_t TK = T * l->K;
+    const int64_t NB = (T + kPermTokens - 1) / kPermTokens;
+    const size_t hbytes = l->wdtype == MOE_DTYPE_F32 ? 4 : 2;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    w.ids = take(TK * 4);
+    w.weights = take(TK * 4);
+    w.block_counts = take(NB * l->E * 4);
+    w.block_base = take(NB * l->E * 4);
+    w.counts = take(l->E * 4);
+    w.offsets = take((l->E + 1) * 4);
+    w.tile_cum1 = take((l->E + 1) * 4);
+    w.tile_cum2 = take((l->E + 1) * 4);
+    w.row_token = take(TK * 4);
+    w.slot_row = take(TK * 4);
+    w.h = take(TK * l->I * hbytes);
+    w.y = take(TK * l->H * 4);
+    w.total = o;
+    return w;
+}
+
+// Kernel variant: f32 layers use the f32 kernels; otherwise the small-M
+// (decode) tiles when the average expert holds few rows.
+enum class Path { kF32, kPrefill, kDecode };
+
+Path choose_path(const moe_layer *l, int64_t T)
+{
+    if (l->wdtype == MOE_DTYPE_F32) return Path::kF32;
+    if (l->opts.gemm_variant == 1) return Path::kPrefill;
+    if (l->opts.gemm_variant == 2) return Path::kDecode;
+    const double rows_per_expert = (double)(T * l->K) / (double)l->E;
+    return rows_per_expert < 96.0 ? Path::kDecode : Path::kPrefill;
+}
+
+int path_bm(Path p)
+{
+    if (p == Path::kF32) return gemm_f32_bm();
+    return gemm_bm(p == Path::kPrefill ? GemmKind::kPrefill : GemmKind::kDecode);
+}
+
+int path_bn(Path p, bool gated)
+{
+    if (p == Path::kF32) return gemm_f32_bn(gated);
+    return gemm_bn(p == Path::kPrefill ? GemmKind::kPrefill : GemmKind::kDecode, gated);
+}
+
+moe_status hip_check(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+int64_t tokens_of(const moe_tensor &t, int64_t last, bool *okp)
+{
+    *okp = false;
+    if (t.ndim < 2 || t.ndim > 3 || t.shape[t.ndim - 1] != last) return 0;
+    int64_t T = 1;
+    for (int i = 0; i < t.ndim - 1; ++i) {
+        if (t.shape[i] < 0) return 0;
+        T *= t.shape[i];
+    }
+    *okp = true;
+    return T;
+}
+
+// Routing + permutation into the workspace.
+moe_status run_route(const moe_layer *l, const float *logits, int64_t T, char *ws,
+                     const Workspace &W, Path path, hipStream_t s, void *const *events)
+{
+    RouteArgs ra{};
+    ra.logits = logits;
+    ra.sel_bias = present(l->w.e_score_correction_bias)
+                      ? (const float *)l->w.e_score_correction_bias.data
+                      : nullptr;
+    ra.ids = (int32_t *)(ws + W.ids);
+    ra.weights = (float *)(ws + W.weights);
+    ra.T = (int)T;
+    ra.E = (int)l->E;
+    ra.K = (int)l->K;
+    ra.scoring = l->opts.scoring;
+    ra.renormalize = l->opts.renormalize;
+    ra.n_group = l->opts.n_group;
+    ra.topk_group = l->opts.topk_group;
+    ra.scale = l->opts.routed_scaling_factor;
+    moe_status st = hip_check(launch_route(ra, s), "route launch");
+    if (st) return st;
+    if (events && events[1] &&
+        (st = hip_check(hipEventRecord((hipEvent_t)events[1], s), "event record")))
+        return st;
+
+    PermuteArgs pa{};
+    pa.ids = ra.ids;
+    pa.T = (int)T;
+    pa.E = (int)l->E;
+    pa.K = (int)l->K;
+    pa.block_counts = (int32_t *)(ws + W.block_counts);
+    pa.block_base = (int32_t *)(ws + W.block_base);
+    pa.counts = (int32_t *)(ws + W.counts);
+    pa.offsets = (int32_t *)(ws + W.offsets);
+    pa.row_token = (int32_t *)(ws + W.row_token);
+    pa.slot_row = (int32_t *)(ws + W.slot_row);
+    pa.tile_cum1 = (int32_t *)(ws + W.tile_cum1);
+    pa.tile_cum2 = (int32_t *)(ws + W.tile_cum2);
+    pa.bm1 = path_bm(path);
+    pa.bm2 = path_bm(path);
+    if ((st = hip_check(launch_permute(pa, s), "permute launch"))) return st;
+    if (events && events[2] &&
+        (st = hip_check(hipEventRecord((hipEvent_t)events[2], s), "event record")))
+        return st;
+    return MOE_OK;
+}
+
+moe_status copy_routing(const moe_layer *l, int64_t T, const char *ws, const Workspace &W,
+                        moe_routing_out *r, hipStream_t s)
+{
+    if (!r) return MOE_OK;
+    const int64_t TK = T * l->K;
+    struct {
+        void *dst;
+        size_t src;
+        size_t bytes;
+    } cp[] = {
+        {r->topk_ids, W.ids, (size_t)TK * 4},
+        {r->topk_weights, W.weights, (size_t)TK * 4},
+        {r->expert_counts, W.counts, (size_t)l->E * 4},
+        {r->expert_offsets, W.offsets, (size_t)(l->E + 1) * 4},
+        {r->row_token, W.row_token, (size_t)TK * 4},
+        {r->slot_row, W.slot_row, (size_t)TK * 4},
+    };
+    for (auto &c : cp) {
+        if (!c.dst || c.bytes == 0) continue;
+        moe_status st = hip_check(
+            hipMemcpyAsync(c.dst, ws + c.src, c.bytes, hipMemcpyDeviceToDevice, s),
+            "routing copy");
+        if (st) return st;
+    }
+    return MOE_OK;
+}
+
+moe_status check_workspace(const moe_layer *l, int64_t T, void *ws, size_t bytes,
+                           Workspace *W)
+{
+    *W = layout(l, T);
+    if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+    if (((uintptr_t)ws & 255) != 0)
+        return fail(MOE_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (bytes < W->total)
+        return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", bytes, W->total);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_options_default(moe_options *o)
+{
+    if (!o) return fail(MOE_ERR_INVALID_ARGUMENT, "options is NULL");
+    std::memset(o, 0, sizeof *o);
+    o->scoring = MOE_SCORING_SOFTMAX;
+    o->renormalize = 0;
+    o->n_group = 0;
+    o->topk_group = 0;
+    o->routed_scaling_factor = 1.0f;
+    o->activation = MOE_ACT_SILU_GATED;
+    o->swiglu_fusion = MOE_FUSION_SPLIT;
+    o->swiglu_alpha = 1.0f;
+    o->swiglu_beta = 0.0f;
+    o->swiglu_limit = 0.0f;
+    o->gemm_variant = 0;
+    return MOE_OK;
+}
+
+moe_status moe_create(int64_t E, int64_t H, int64_t I, int64_t K, moe_dtype wdtype,
+                      int has_gu_bias, int has_d_bias, const moe_options *opts,
+                      moe_layer **out)
+{
+    if (!out) return fail(MOE_ERR_INVALID_ARGUMENT, "out_layer is NULL");
+    *out = nullptr;
+    moe_options o;
+    if (opts) o = *opts;
+    else moe_options_default(&o);
+    if (E < 1 || E > kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "num_experts %lld outside 1..%d", (long long)E,
+                    kMaxExperts);
+    if (K < 1 || K > E || K > kMaxTopK)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "top_k %lld outside 1..min(E, %d)", (long long)K,
+                    kMaxTopK);
+    if (H < 1 || I < 1 || H > (1 << 20) || I > (1 << 20))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "hidden/intermediate size out of range");
+    if (wdtype != MOE_DTYPE_F32 && wdtype != MOE_DTYPE_BF16 && wdtype != MOE_DTYPE_MXFP4)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "weight dtype must be F32, BF16 or MXFP4");
+    if (wdtype == MOE_DTYPE_MXFP4 && (H % 32 || I % 32))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "MXFP4 needs H and I multiples of 32");
+    if (H % 8 || I % 8)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "H and I must be multiples of 8");
+    if (o.scoring != MOE_SCORING_SOFTMAX && o.scoring != MOE_SCORING_SIGMOID)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "unknown scoring %d", o.scoring);
+    if (o.n_group < 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "n_group < 0");
+    if (o.n_group > 0) {
+        if (o.n_group > kMaxGroups || E % o.n_group)
+            return fail(MOE_ERR_INVALID_ARGUMENT, "n_group must divide E and be <= %d",
+                        kMaxGroups);
+        if (o.topk_group < 1 || o.topk_group > o.n_group)
+            return fail(MOE_ERR_INVALID_ARGUMENT, "topk_group outside 1..n_group");
+        if (K > (int64_t)o.topk_group * (E / o.n_group))
+            return fail(MOE_ERR_INVALID_ARGUMENT,
+                        "top_k exceeds the experts of topk_group groups");
+    }
+    if (o.activation != MOE_ACT_SILU_GATED && o.activation != MOE_ACT_SWIGLU_CLAMPED)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "unknown activation %d", o.activation);
+    if (o.swiglu_fusion < MOE_FUSION_NONE || o.swiglu_fusion > MOE_FUSION_SPLIT)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "unknown swiglu_fusion %d", o.swiglu_fusion);
+    if (o.gemm_variant < 0 || o.gemm_variant > 2)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "unknown gemm_variant %d", o.gemm_variant);
+    if (!(o.routed_scaling_factor == o.routed_scaling_factor))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "routed_scaling_factor is NaN");
+    moe_layer *l = new (std::nothrow) moe_layer();
+    if (!l) return fail(MOE_ERR_INVALID_ARGUMENT, "out of host memory");
+    l->E = E;
+    l->H = H;
+    l->I = I;
+    l->K = K;
+    l->wdtype = wdtype;
+    l->has_gu_bias = has_gu_bias ? 1 : 0;
+    l->has_d_bias = has_d_bias ? 1 : 0;
+    l->opts = o;
+    l->bound = false;
+    *out = l;
+    return MOE_OK;
+}
+
+moe_status moe_set_weights(moe_layer *l, const moe_weights *w)
+{
+    if (!l || !w) return fail(MOE_ERR_INVALID_ARGUMENT, "layer or weights is NULL");
+    const int64_t E = l->E, H = l->H, I = l->I;
+    const int wd = l->wdtype, ad = act_dtype(l);
+    const bool fz = fused(l);
+    moe_status st;
+    if (!present(w->gate_up_experts) || !present(w->down_experts))
+        return fail(MOE_ERR_SHAPE_MISMATCH, "gate_up_experts and down_experts are required");
+    if ((st = check_tensor("gate_up_experts", w->gate_up_experts, wd, {E, fz ? 2 * I : I, H})))
+        return st;
+    if ((st = check_tensor("down_experts", w->down_experts, wd, {E, H, I}))) return st;
+    if (fz && present(w->gate_experts))
+        return fail(MOE_ERR_SHAPE_MISMATCH, "gate_experts given for a fused gate||up layout");
+    if (!fz) {
+        if (!present(w->gate_experts))
+            return fail(MOE_ERR_SHAPE_MISMATCH,
+                        "gate_experts is required when swiglu_fusion = NONE");
+        if ((st = check_tensor("gate_experts", w->gate_experts, wd, {E, I, H}))) return st;
+    }
+    if (present(w->gate_up_bias)) {
+        if (!l->has_gu_bias)
+            return fail(MOE_ERR_NOT_DECLARED, "gate_up_bias given but not declared");
+        if ((st = check_tensor("gate_up_bias", w->gate_up_bias, ad, {E, fz ? 2 * I : I})))
+            return st;
+    }
+    if (present(w->gate_bias)) {
+        if (!l->has_gu_bias)
+            return fail(MOE_ERR_NOT_DECLARED, "gate_bias given but not declared");
+        if (fz)
+            return fail(MOE_ERR_SHAPE_MISMATCH, "gate_bias given for a fused gate||up layout");
+        if ((st = check_tensor("gate_bias", w->gate_bias, ad, {E, I}))) return st;
+    }
+    if (present(w->down_bias)) {
+        if (!l->has_d_bias)
+            return fail(MOE_ERR_NOT_DECLARED, "down_bias given but not declared");
+        if ((st = check_tensor("down_bias", w->down_bias, ad, {E, H}))) return st;
+    }
+    if (present(w->e_score_correction_bias) &&
+        (st = check_tensor("e_score_correction_bias", w->e_score_correction_bias,
+                           MOE_DTYPE_F32, {E})))
+        return st;
+    l->w = *w;
+    l->bound = true;
+    return MOE_OK;
+}
+
+moe_status moe_prepare(moe_layer *l, void *stream)
+{
+    (void)stream;
+    if (!l) return fail(MOE_ERR_INVALID_ARGUMENT, "layer is NULL");
+    return check_bound(l);
+}
+
+moe_status moe_workspace_size(const moe_layer *l, int64_t T, size_t *bytes)
+{
+    if (!l || !bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "layer or bytes is NULL");
+    if (T < 0 || T > (1 << 24)) return fail(MOE_ERR_INVALID_ARGUMENT, "T out of range");
+    *bytes = layout(l, T).total;
+    return MOE_OK;
+}
+
+moe_status moe_route(const moe_layer *l, const moe_tensor *logits, moe_routing_out *r,
+                     void *ws, size_t ws_bytes, void *stream)
+{
+    if (!l || !logits || !r) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL argument");
+    bool okT;
+    const int64_t T = tokens_of(*logits, l->E, &okT);
+    if (!okT || logits->dtype != MOE_DTYPE_F32)
+        return fail(MOE_ERR_SHAPE_MISMATCH, "router_logits must be f32 [T, E]");
+    if (T > (1 << 24)) return fail(MOE_ERR_INVALID_ARGUMENT, "T out of range");
+    if (T == 0) return MOE_OK;
+    if (!logits->data) return fail(MOE_ERR_INVALID_ARGUMENT, "router_logits data is NULL");
+    Workspace W;
+    moe_status st = check_workspace(l, T, ws, ws_bytes, &W);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const Path path = choose_path(l, T);
+    if ((st = run_route(l, (const float *)logits->data, T, (char *)ws, W, path, s, nullptr)))
+        return st;
+    return copy_routing(l, T, (const char *)ws, W, r, s);
+}
+
+moe_status moe_forward(const moe_layer *l, const moe_tensor *x, const moe_tensor *logits,
+                       const moe_tensor *shared, moe_tensor *out, void *ws, size_t ws_bytes,
+                       moe_routing_out *routing, void *stream)
+{
+    return moe_forward_timed(l, x, logits, shared, out, ws, ws_bytes, routing, stream, nullptr);
+}
+
+moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_tensor *logits,
+                             const moe_tensor *shared, moe_tensor *out, void *ws,
+                             size_t ws_bytes, moe_routing_out *routing, void *stream,
+                             void *const *events)
+{
+    if (!l || !x || !logits || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL argument");
+    moe_status st = check_bound(l);
+    if (st) return st;
+    const int ad = act_dtype(l);
+    if (x->dtype != MOE_DTYPE_F32 && x->dtype != MOE_DTYPE_BF16)
+        return fail(MOE_ERR_SHAPE_MISMATCH, "x dtype must be f32 or bf16");
+    if (x->dtype != ad)
+        return fail(MOE_ERR_UNSUPPORTED, "x dtype %s with %s weights (needs %s)",
+                    dtype_name(x->dtype), dtype_name(l->wdtype), dtype_name(ad));
+    bool okT;
+    const int64_t T = tokens_of(*x, l->H, &okT);
+    if (!okT) return fail(MOE_ERR_SHAPE_MISMATCH, "x must be [T, H] or [B, S, H]");
+    bool okL;
+    const int64_t TL = tokens_of(*logits, l->E, &okL);
+    if (!okL || TL != T || logits->dtype != MOE_DTYPE_F32)
+        return fail(MOE_ERR_SHAPE_MISMATCH, "router_logits must be f32 [T, E] with T = %lld",
+                    (long long)T);
+    auto same_as_x = [&](const moe_tensor &t) {
+        if (t.dtype != x->dtype || t.ndim != x->ndim) return false;
+        for (int i = 0; i < x->ndim; ++i)
+            if (t.shape[i] != x->shape[i]) return false;
+        return true;
+    };
+    if (!same_as_x(*out)) return fail(MOE_ERR_SHAPE_MISMATCH, "out must match x's shape and dtype");
+    const bool has_shared = shared && present(*shared);
+    if (has_shared && !same_as_x(*shared))
+        return fail(MOE_ERR_SHAPE_MISMATCH, "shared_output must match x's shape and dtype");
+    if (T > (1 << 24)) return fail(MOE_ERR_INVALID_ARGUMENT, "T out of range");
+    if (T == 0) return MOE_OK;
+    if (!x->data || !logits->data || !out->data)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "x, router_logits or out data is NULL");
+    Workspace W;
+    if ((st = check_workspace(l, T, ws, ws_bytes, &W))) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    char *wsb = (char *)ws;
+    auto mark = [&](int i) -> moe_status {
+        if (events && events[i])
+            return hip_check(hipEventRecord((hipEvent_t)events[i], s), "event record");
+        return MOE_OK;
+    };
+    const Path path = choose_path(l, T);
+    if ((st = mark(0))) return st;
+    if ((st = run_route(l, (const float *)logits->data, T, wsb, W, path, s, events))) return st;
+
+    const int64_t TK = T * l->K;
+    const int bm = path_bm(path);
+    const int64_t max_m_tiles = (TK + bm - 1) / bm + (l->E < TK ? l->E : TK);
+    const bool mx = l->wdtype == MOE_DTYPE_MXFP4;
+    const bool fz = fused(l);
+
+    // GEMM 1: gate||up with the fused activation -> h
+    GemmArgs g1{};
+    g1.a = x->data;
+    g1.row_token = (const int32_t *)(wsb + W.row_token);
+    g1.counts = (const int32_t *)(wsb + W.counts);
+    g1.offsets = (const int32_t *)(wsb + W.offsets);
+    g1.tile_cum = (const int32_t *)(wsb + W.tile_cum1);
+    g1.E = (int)l->E;
+    g1.Kd = (int)l->H;
+    g1.Nout = (int)l->I;
+    const int bn1 = path_bn(path, true);
+    g1.nN = (int)((l->I + bn1 - 1) / bn1);
+    g1.out = wsb + W.h;
+    g1.act = l->opts.activation;
+    g1.alpha = l->opts.swiglu_alpha;
+    g1.beta = l->opts.swiglu_beta;
+    g1.limit = l->opts.swiglu_limit;
+    WeightRows &w1 = g1.w;
+    if (fz) {
+        w1.w_gate = w1.w_up = l->w.gate_up_experts.data;
+        w1.s_gate = w1.s_up = l->w.gate_up_experts.scales;
+        w1.e_rows = 2 * l->I;
+        if (l->opts.swiglu_fusion == MOE_FUSION_INTERLEAVED) {
+            w1.row_mul = 2;
+            w1.off_gate = 0;
+            w1.off_up = 1;
+        } else {
+            w1.row_mul = 1;
+            w1.off_gate = 0;
+            w1.off_up = (int)l->I;
+        }
+        if (present(l->w.gate_up_bias)) w1.b_gate = w1.b_up = l->w.gate_up_bias.data;
+    } else {
+        w1.w_gate = l->w.gate_experts.data;
+        w1.s_gate = l->w.gate_experts.scales;
+        w1.w_up = l->w.gate_up_experts.data;
+        w1.s_up = l->w.gate_up_experts.scales;
+        w1.e_rows = l->I;
+        w1.row_mul = 1;
+        w1.off_gate = w1.off_up = 0;
+        if (present(l->w.gate_bias)) w1.b_gate = l->w.gate_bias.data;
+        if (present(l->w.gate_up_bias)) w1.b_up = l->w.gate_up_bias.data;
+    }
+
+    // GEMM 2: down + bias -> y (f32)
+    GemmArgs g2{};
+    g2.a = wsb + W.h;
+    g2.row_token = nullptr;
+    g2.counts = g1.counts;
+    g2.offsets = g1.offsets;
+    g2.tile_cum = (const int32_t *)(wsb + W.tile_cum2);
+    g2.E = (int)l->E;
+    g2.Kd = (int)l->I;
+    g2.Nout = (int)l->H;
+    const int bn2 = path_bn(path, false);
+    g2.nN = (int)((l->H + bn2 - 1) / bn2);
+    g2.out = wsb + W.y;
+    g2.w.w_gate = l->w.down_experts.data;
+    g2.w.s_gate = l->w.down_experts.scales;
+    g2.w.e_rows = l->H;
+    g2.w.row_mul = 1;
+    if (present(l->w.down_bias)) g2.w.b_gate = l->w.down_bias.data;
+
+    if (max_m_tiles * (g1.nN > g2.nN ? g1.nN : g2.nN) + 8 > 0x7fffffffLL)
+        return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch");
+
+    if (path == Path::kF32) {
+        if ((st = hip_check(launch_gemm_f32(true, g1, max_m_tiles, s), "gemm1 launch"))) return st;
+        if ((st = mark(3))) return st;
+        if ((st = hip_check(launch_gemm_f32(false, g2, max_m_tiles, s), "gemm2 launch"))) return st;
+    } else {
+        const GemmKind kind = path == Path::kPrefill ? GemmKind::kPrefill : GemmKind::kDecode;
+        if ((st = hip_check(launch_gemm_bf16(kind, true, mx, g1, max_m_tiles, s), "gemm1 launch")))
+            return st;
+        if ((st = mark(3))) return st;
+        if ((st = hip_check(launch_gemm_bf16(kind, false, mx, g2, max_m_tiles, s),
+                            "gemm2 launch")))
+            return st;
+    }
+    if ((st = mark(4))) return st;
+
+    CombineArgs ca{};
+    ca.y = (const float *)(wsb + W.y);
+    ca.weights = (const float *)(wsb + W.weights);
+    ca.slot_row = (const int32_t *)(wsb + W.slot_row);
+    ca.shared = has_shared ? shared->data : nullptr;
+    ca.out = (void *)out->data;
+    ca.T = (int)T;
+    ca.H = (int)l->H;
+    ca.K = (int)l->K;
+    ca.out_bf16 = x->dtype == MOE_DTYPE_BF16;
+    if ((st = hip_check(launch_combine(ca, s), "combine launch"))) return st;
+    if ((st = mark(5))) return st;
+    return copy_routing(l, T, wsb, W, routing, s);
+}
+
+moe_status moe_destroy(moe_layer *l)
+{
+    delete l;
+    return MOE_OK;
+}
+
+const char *moe_last_error(void)
+{
+    return g_err.c_str();
+}
+
+const char *moe_status_string(moe_status s)
+{
+    switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_SHAPE_MISMATCH: return "MOE_ERR_SHAPE_MISMATCH";
+    case MOE_ERR_NOT_DECLARED: return "MOE_ERR_NOT_DECLARED";
+    case MOE_ERR_UNBOUND: return "MOE_ERR_UNBOUND";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Internal launch interface between the C-ABI host code (api.cpp) and the
+// HIP kernels.  Not installed; the public boundary is include/moe_mi355x.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Upper limits the kernels are written for (checked by the host before launch).
+constexpr int kMaxExperts = 1024;   // routing keeps E/64 experts per lane
+constexpr int kMaxTopK = 64;        // one lane per kept slot
+constexpr int kMaxGroups = 64;      // one lane per group score
+constexpr int kPermTokens = 256;    // tokens per permutation block
+
+struct RouteArgs {
+    const float *logits;     // [T, E]
+    const float *sel_bias;   // [E] or null
+    int32_t *ids;            // [T, K]
+    float *weights;          // [T, K]
+    int T, E, K;
+    int scoring;             // 0 softmax, 1 sigmoid
+    int renormalize;
+    int n_group, topk_group;
+    float scale;             // routed scaling factor
+};
+
+struct PermuteArgs {
+    const int32_t *ids;      // [T, K]
+    int T, E, K;
+    int32_t *block_counts;   // [NB, E]   NB = ceil(T / kPermTokens)
+    int32_t *block_base;     // [NB, E]
+    int32_t *counts;         // [E]
+    int32_t *offsets;        // [E + 1]
+    int32_t *row_token;      // [T*K]
+    int32_t *slot_row;       // [T*K]
+    int32_t *tile_cum1;      // [E + 1] cumulative M-tiles of GEMM 1
+    int32_t *tile_cum2;      // [E + 1] cumulative M-tiles of GEMM 2
+    int bm1, bm2;            // token-tile heights of the two GEMMs
+};
+
+// Weight-operand description of one grouped GEMM.  Feature row c of expert e
+// lives at row (e * e_rows + c * row_mul + off) of the stack whose base is
+// w_gate (gate / only operand) or w_up (up operand of the gated GEMM).
+struct WeightRows {
+    const void *w_gate;          // element base (bf16 / f32) or MXFP4 codes
+    const void *w_up;
+    const uint8_t *s_gate;       // MXFP4 scales (same row mapping), else null
+    const uint8_t *s_up;
+    int64_t e_rows;              // rows per expert slab
+    int row_mul;                 // 2 for interleaved gate||up, else 1
+    int off_gate, off_up;        // row offsets of the gate / up operands
+    const void *b_gate;          // bias (x dtype), indexed like the rows; or null
+    const void *b_up;
+};
+
+struct GemmArgs {
+    const void *a;               // activations: x [T, Kd] or h [T*K, Kd]
+    const int32_t *row_token;    // if set, A row r reads a[row_token[r]]
+    WeightRows w;
+    const int32_t *counts;       // [E]
+    const int32_t *offsets;      // [E + 1]
+    const int32_t *tile_cum;     // [E + 1] cumulative M-tiles at this BM
+    int E;
+    int Kd;                      // reduction length
+    int Nout;                    // output features: I (gated) or H (down)
+    int nN;                      // feature tiles
+    void *out;                   // h bf16 [T*K, I] or y f32 [T*K, H]
+    int act;                     // 0 SiLU-gated, 1 clamped SwiGLU
+    float alpha, beta, limit;
+};
+
+struct CombineArgs {
+    const float *y;              // [T*K, H] (row order of the permutation)
+    const float *weights;        // [T, K]
+    const int32_t *slot_row;     // [T, K]
+    const void *shared;          // [T, H] x dtype or null
+    void *out;                   // [T, H] x dtype
+    int T, H, K;
+    int out_bf16;                // 1: bf16 x/out, 0: f32
+};
+
+// Dense f32 grouped GEMM (the fp32 layer): same contract as GemmArgs with
+// f32 operands.
+hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+hipError_t launch_permute(const PermuteArgs &a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+
+// Grouped-GEMM variants.  `gated` selects the gate||up GEMM with the fused
+// activation (bf16 h out) versus the down GEMM (+bias, f32 y out).
+enum class GemmKind { kPrefill = 0, kDecode = 1 };
+int gemm_bm(GemmKind kind);          // token-tile height of a variant
+int gemm_bn(GemmKind kind, bool gated);   // output features per tile
+hipError_t launch_gemm_bf16(GemmKind kind, bool gated, bool mxfp4,
+                            const GemmArgs &a, int64_t max_m_tiles, hipStream_t s);
+int gemm_f32_bm();
+int gemm_f32_bn(bool gated);
+hipError_t launch_gemm_f32(bool gated, const GemmArgs &a, int64_t max_m_tiles,
+                           hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,227 @@
+// Router top-K: one 64-lane wavefront per token.
+//
+// Semantics (logicaffeine "MoeSpec" fields `score`, `selection_bias`,
+// `groups`, `renormalize`, `scale`, method `sum_can_clamp`; "Moe" fields
+// `norm_top_k`, `weights_scale`, `groups`; graiphic ONNX "MoE" attribute `k`):
+//   score   softmax over every logit, or each logit's own sigmoid;
+//   key     score + selection bias (selection only);
+//   groups  E split into n_group equal contiguous groups, each scored by the
+//           sum of its two best keys; experts outside the topk_group best
+//           groups are ineligible;
+//   top-K   the K largest eligible keys in rank order, equal keys toward the
+//           lower expert index (lower group index for groups);
+//   weight  the kept scores, renormalised by max(sum, 2^-14) when asked,
+//           then times the routed scale.
+// Scores, keys, group sums and weights are computed in fp64 so that the
+// discrete choices agree with an fp64 reference except at fp64 near-ties;
+// the weights are stored as f32.
+//
+// Lane layout: lane l holds experts l, l+64, l+128, ... (coalesced logit
+// loads); argmax steps are butterfly shuffles across the wavefront.
+// Every argmax runs over a set that still holds a candidate (validated
+// options guarantee >= K eligible experts), and a NaN key counts as -inf, so
+// every stored id is a real expert index.
+#include "moe_kernels.h"
+
+#include <math.h>
+
+namespace moe {
+namespace {
+
+struct KeyIdx {
+    double key;
+    int idx;
+};
+
+// (key, idx) is better than (k2, i2) when its key is larger or, on equal
+// keys, its index is lower.  Missing entries carry key = -inf, idx = INT_MAX.
+__device__ inline bool better(double k1, int i1, double k2, int i2)
+{
+    return k1 > k2 || (k1 == k2 && i1 < i2);
+}
+
+__device__ inline KeyIdx wave_argmax(KeyIdx v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        double ok = __shfl_xor(v.key, off, 64);
+        int oi = __shfl_xor(v.idx, off, 64);
+        if (better(ok, oi, v.key, v.idx)) {
+            v.key = ok;
+            v.idx = oi;
+        }
+    }
+    return v;
+}
+
+__device__ inline double wave_max(double v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v = fmax(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ inline double wave_sum(double v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+constexpr int kNone = 0x7fffffff;
+
+template <int EPL>
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.T) return;   // whole wavefront leaves together
+    const int E = a.E;
+    const float *lg = a.logits + (int64_t)t * E;
+
+    double score[EPL], key[EPL];
+    bool live[EPL];   // a real expert, eligible and not yet taken
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        live[i] = e < E;
+        score[i] = live[i] ? (double)lg[e] : -INFINITY;
+    }
+
+    // scores
+    if (a.scoring == 0) {
+        double m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) m = fmax(m, score[i]);
+        m = wave_max(m);
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            score[i] = live[i] ? exp(score[i] - m) : 0.0;
+            s += score[i];
+        }
+        s = wave_sum(s);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) score[i] = score[i] / s;
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            score[i] = live[i] ? 1.0 / (1.0 + exp(-score[i])) : 0.0;
+    }
+
+    // selection keys
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = live[i] ? (a.sel_bias ? score[i] + (double)a.sel_bias[e] : score[i])
+                         : -INFINITY;
+        if (key[i] != key[i]) key[i] = -INFINITY;   // NaN input: never preferred
+    }
+
+    // group limit
+    if (a.n_group > 0) {
+        const int gs = E / a.n_group;
+        double my_gscore = -INFINITY;   // lane g holds the score of group g
+        for (int g = 0; g < a.n_group; ++g) {
+            KeyIdx b1{-INFINITY, kNone};
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane + 64 * i;
+                if (live[i] && e / gs == g && better(key[i], e, b1.key, b1.idx))
+                    b1 = KeyIdx{key[i], e};
+            }
+            b1 = wave_argmax(b1);
+            double gsum = b1.key;
+            if (gs >= 2) {
+                KeyIdx b2{-INFINITY, kNone};
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) {
+                    const int e = lane + 64 * i;
+                    if (live[i] && e / gs == g && e != b1.idx &&
+                        better(key[i], e, b2.key, b2.idx))
+                        b2 = KeyIdx{key[i], e};
+                }
+                b2 = wave_argmax(b2);
+                gsum = b1.key + b2.key;
+                if (gsum != gsum) gsum = -INFINITY;
+            }
+            if (lane == g) my_gscore = gsum;
+        }
+        uint64_t kept = 0;
+        for (int r = 0; r < a.topk_group; ++r) {
+            KeyIdx c{lane < a.n_group && !((kept >> lane) & 1) ? my_gscore : -INFINITY,
+                     lane < a.n_group && !((kept >> lane) & 1) ? lane : kNone};
+            c = wave_argmax(c);
+            kept |= 1ull << c.idx;
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            if (live[i] && !((kept >> (e / gs)) & 1)) live[i] = false;
+        }
+    }
+
+    // top-K; lane j keeps slot j
+    int my_id = 0;
+    double my_w = 0.0;
+    for (int j = 0; j < a.K; ++j) {
+        KeyIdx c{-INFINITY, kNone};
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            if (live[i] && better(key[i], e, c.key, c.idx)) c = KeyIdx{key[i], e};
+        }
+        c = wave_argmax(c);
+        const int owner = c.idx & 63, slot = c.idx >> 6;
+        double sc = 0.0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (i == slot) sc = score[i];
+        sc = __shfl(sc, owner, 64);
+        if (lane == owner) {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (i == slot) live[i] = false;
+        }
+        if (lane == j) {
+            my_id = c.idx;
+            my_w = sc;
+        }
+    }
+
+    // weights: renormalise (sum in slot order, clamped at 2^-14), then scale
+    if (a.renormalize) {
+        double s = 0.0;
+        for (int j = 0; j < a.K; ++j) s += __shfl(my_w, j, 64);
+        const double d = s > 0x1p-14 ? s : 0x1p-14;
+        my_w = my_w / d;
+    }
+    my_w = my_w * (double)a.scale;
+    if (lane < a.K) {
+        a.ids[(int64_t)t * a.K + lane] = my_id;
+        a.weights[(int64_t)t * a.K + lane] = (float)my_w;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t s)
+{
+    const dim3 grid((a.T + 3) / 4), block(256);
+    const int epl = (a.E + 63) / 64;
+    if (epl <= 1)
+        route_kernel<1><<<grid, block, 0, s>>>(a);
+    else if (epl <= 2)
+        route_kernel<2><<<grid, block, 0, s>>>(a);
+    else if (epl <= 4)
+        route_kernel<4><<<grid, block, 0, s>>>(a);
+    else if (epl <= 8)
+        route_kernel<8><<<grid, block, 0, s>>>(a);
+    else
+        route_kernel<16><<<grid, block, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,98 @@
+"""Shared helpers of the GPU parity tests: run the HIP layer, run the oracle
+on host copies of the same inputs, compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from mixture_experts_ffn_03_amd import from_config
+
+# max |err| <= TOL * RMS(out): 1e-4 for f32 layers, 2e-2 for bf16 / MXFP4
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+EXPERT_SLOTS = ("gate_up_experts", "gate_up_scales", "down_experts", "down_scales",
+                "gate_experts", "gate_scales", "gate_up_bias", "down_bias", "gate_bias")
+
+
+def host(inp: dict) -> dict:
+    return {k: v.cpu() for k, v in inp.items()}
+
+
+def host_experts(inp: dict, experts) -> dict:
+    """Host copies in which only the given experts' slabs are filled (the
+    oracle reads no other expert)."""
+    out = {}
+    ex = sorted(set(int(e) for e in experts))
+    for k, v in inp.items():
+        if k in EXPERT_SLOTS:
+            h = torch.empty(v.shape, dtype=v.dtype)
+            for e in ex:
+                h[e] = v[e].cpu()
+            out[k] = h
+        else:
+            out[k] = v.cpu()
+    return out
+
+
+def run_gpu(cfg, inp: dict, routing: bool = True, **over):
+    layer = from_config(cfg, **over)
+    layer.set_weights_from(inp)
+    T = inp["x"].shape[0] if inp["x"].dim() == 2 else inp["x"].numel() // cfg.H
+    r = layer.routing_buffers(T, cfg.E, cfg.K, inp["x"].device) if routing else None
+    out = layer(inp["x"], inp["logits"], inp.get("shared_output"), routing=r)
+    torch.cuda.synchronize()
+    return out, r, layer
+
+
+def compare_out(out_gpu: torch.Tensor, ref: np.ndarray, x_dtype: str, what: str = ""):
+    """Max-abs error against the fp64 oracle, relative to the oracle RMS.
+    Also reports the floor set by rounding the oracle itself to x's dtype."""
+    o = out_gpu.float().cpu().numpy().astype(np.float64).reshape(ref.shape)
+    rms = float(np.sqrt((ref ** 2).mean()))
+    err = float(np.abs(o - ref).max())
+    floor = 0.0
+    if x_dtype == "bf16":
+        rb = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+        floor = float(np.abs(rb - ref).max())
+    rel = err / rms if rms > 0 else err
+    print(f"[parity] {what}: max|err|/rms = {rel:.3e} (bf16 rounding floor "
+          f"{floor / rms if rms else 0:.3e}, rms {rms:.4g})", flush=True)
+    assert np.isfinite(o).all(), what
+    assert err <= TOL[x_dtype] * rms, (what, rel)
+    return rel
+
+
+def check_routing(cfg, inp: dict, r: dict, T: int):
+    """ids, counts, offsets and the permutation bit-exact; weights to f32
+    rounding of the fp64 oracle weights."""
+    p = oracle.params_of(cfg, T=T)
+    ro = oracle.route(p, inp["logits"].cpu(),
+                      inp["e_score_correction_bias"].cpu()
+                      if "e_score_correction_bias" in inp else None)
+    ids = r["topk_ids"].cpu().numpy()
+    if not (ids == ro["ids"]).all():
+        bad = np.argwhere((ids != ro["ids"]).any(1))[:5, 0]
+        msg = []
+        for t in bad:
+            keys = ro["keys"][t]
+            srt = np.sort(keys[np.isfinite(keys)])[::-1]
+            margin = srt[cfg.K - 1] - srt[cfg.K] if len(srt) > cfg.K else np.inf
+            msg.append(f"t={t} gpu={ids[t].tolist()} oracle={ro['ids'][t].tolist()} "
+                       f"fp64 margin at K={margin:.3e}")
+        raise AssertionError("routing ids differ:\n" + "\n".join(msg))
+    w = r["topk_weights"].cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(w, ro["weights"], rtol=3e-7, atol=1e-38)
+    pr = oracle.permute(p, ro["ids"])
+    assert (r["expert_counts"].cpu().numpy() == pr["counts"]).all()
+    assert (r["expert_offsets"].cpu().numpy() == pr["offsets"]).all()
+    assert (r["row_token"].cpu().numpy() == pr["row_token"]).all()
+    assert (r["slot_row"].cpu().numpy() == pr["slot_row"]).all()
+    return ro
+
+
+def sample_tokens(T: int, n: int, seed: int = 7) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    base = {0, T - 1, T // 2}
+    base |= set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    return np.array(sorted(base))[: max(n, 3)]

@@ -1,0 +1,181 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launched).
+
+The library must load, export every function include/moe_mi355x.h declares,
+and reject bad declarations / bindings / calls with the documented status
+codes before touching the device (clika "ClikaRT::nn::QMoEWoQ": errors on a
+geometry mismatch, a bias without its declared slot, a still-unbound slot).
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from mixture_experts_ffn_03_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from mixture_experts_ffn_03_amd import build
+        build.build()
+    return _lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 10, names
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+    assert sorted(L.EXPORTS) == names
+
+
+def test_status_strings(L):
+    for code, name in L.STATUS_NAMES.items():
+        assert L.lib().moe_status_string(code).decode() == name
+
+
+def test_options_default(L):
+    o = L.options()
+    assert (o.scoring, o.renormalize, o.n_group, o.topk_group) == (0, 0, 0, 0)
+    assert o.routed_scaling_factor == 1.0
+    assert (o.activation, o.swiglu_fusion) == (0, 2)
+    assert (o.swiglu_alpha, o.swiglu_beta, o.swiglu_limit) == (1.0, 0.0, 0.0)
+
+
+def create(L, E=8, H=64, I=32, K=2, dtype="bf16", gub=False, db=False, **opt):
+    h = C.c_void_p()
+    o = L.options(**opt)
+    st = L.lib().moe_create(E, H, I, K, L.WDTYPE[dtype], int(gub), int(db), C.byref(o),
+                            C.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw", [
+    dict(K=9), dict(K=0), dict(E=0), dict(E=2048), dict(K=65, E=128),
+    dict(H=60), dict(dtype="mxfp4", H=48), dict(n_group=3, topk_group=1),
+    dict(n_group=4, topk_group=5), dict(n_group=4, topk_group=1, K=3),
+    dict(n_group=128, E=256, topk_group=1, K=1), dict(scoring=7),
+    dict(activation=5), dict(swiglu_fusion=3)])
+def test_create_rejects_bad_geometry(L, kw):
+    st, h = create(L, **kw)
+    assert st == 1, L.lib().moe_last_error()
+    assert not h.value
+
+
+def _t(L, shape, dtype, ptr=0x1000, scales=None):
+    m = L.moe_tensor()
+    m.data = ptr
+    m.dtype = dtype
+    m.ndim = len(shape)
+    for i, d in enumerate(shape):
+        m.shape[i] = d
+    if scales:
+        m.scales = scales
+    return m
+
+
+def test_set_weights_validation(L):
+    st, h = create(L, gub=True)
+    assert st == 0
+    lib = L.lib()
+    BF = L.MOE_DTYPE_BF16
+    w = L.moe_weights()
+    # forward/prepare before binding: UNBOUND
+    assert lib.moe_prepare(h, None) == 4
+    w.gate_up_experts = _t(L, [8, 64, 64], BF)
+    w.down_experts = _t(L, [8, 64, 32], BF)
+    assert lib.moe_set_weights(h, C.byref(w)) == 0
+    assert lib.moe_prepare(h, None) == 4        # declared gate_up_bias unbound
+    w.gate_up_bias = _t(L, [8, 64], BF)
+    assert lib.moe_set_weights(h, C.byref(w)) == 0
+    assert lib.moe_prepare(h, None) == 0
+    w.down_bias = _t(L, [8, 64], BF)            # not declared
+    assert lib.moe_set_weights(h, C.byref(w)) == 3
+    w.down_bias = L.moe_tensor()
+    w.e_score_correction_bias = _t(L, [8], L.MOE_DTYPE_F32)   # always bindable
+    assert lib.moe_set_weights(h, C.byref(w)) == 0
+    w.gate_up_experts = _t(L, [8, 63, 64], BF)                # geometry mismatch
+    assert lib.moe_set_weights(h, C.byref(w)) == 2
+    w.gate_up_experts = _t(L, [8, 64, 64], L.MOE_DTYPE_F32)   # dtype mismatch
+    assert lib.moe_set_weights(h, C.byref(w)) == 2
+    w.gate_up_experts = _t(L, [8, 64, 64], BF)
+    w.gate_experts = _t(L, [8, 32, 64], BF)                   # unfused slot on fused layout
+    assert lib.moe_set_weights(h, C.byref(w)) == 2
+    lib.moe_destroy(h)
+
+
+def test_unfused_and_mxfp4_binding(L):
+    lib = L.lib()
+    st, h = create(L, dtype="mxfp4", swiglu_fusion="unfused")
+    assert st == 0
+    MX = L.MOE_DTYPE_MXFP4
+    w = L.moe_weights()
+    w.gate_up_experts = _t(L, [8, 32, 64], MX, scales=0x2000)
+    w.down_experts = _t(L, [8, 64, 32], MX, scales=0x3000)
+    assert lib.moe_set_weights(h, C.byref(w)) == 2            # gate_experts missing
+    w.gate_experts = _t(L, [8, 32, 64], MX)                   # no scales
+    assert lib.moe_set_weights(h, C.byref(w)) == 2
+    w.gate_experts = _t(L, [8, 32, 64], MX, scales=0x4000)
+    assert lib.moe_set_weights(h, C.byref(w)) == 0
+    assert lib.moe_prepare(h, None) == 0
+    lib.moe_destroy(h)
+
+
+def test_forward_argument_errors_before_launch(L):
+    lib = L.lib()
+    st, h = create(L)
+    BF, F32 = L.MOE_DTYPE_BF16, L.MOE_DTYPE_F32
+    x = _t(L, [5, 64], BF)
+    lg = _t(L, [5, 8], F32)
+    out = _t(L, [5, 64], BF)
+    ws = C.c_void_p(0x10000)
+    # unbound
+    assert lib.moe_forward(h, C.byref(x), C.byref(lg), None, C.byref(out), ws, 1 << 30,
+                           None, None) == 4
+    w = L.moe_weights()
+    w.gate_up_experts = _t(L, [8, 64, 64], BF)
+    w.down_experts = _t(L, [8, 64, 32], BF)
+    assert lib.moe_set_weights(h, C.byref(w)) == 0
+    bad_lg = _t(L, [4, 8], F32)
+    assert lib.moe_forward(h, C.byref(x), C.byref(bad_lg), None, C.byref(out), ws, 1 << 30,
+                           None, None) == 2
+    xf = _t(L, [5, 64], F32)
+    assert lib.moe_forward(h, C.byref(xf), C.byref(lg), None, C.byref(xf), ws, 1 << 30,
+                           None, None) == 5                   # f32 x with bf16 weights
+    bad_out = _t(L, [5, 64], F32)
+    assert lib.moe_forward(h, C.byref(x), C.byref(lg), None, C.byref(bad_out), ws, 1 << 30,
+                           None, None) == 2
+    bad_sh = _t(L, [5, 32], BF)
+    assert lib.moe_forward(h, C.byref(x), C.byref(lg), C.byref(bad_sh), C.byref(out), ws,
+                           1 << 30, None, None) == 2
+    n = C.c_size_t()
+    assert lib.moe_workspace_size(h, 5, C.byref(n)) == 0 and n.value > 0
+    assert lib.moe_forward(h, C.byref(x), C.byref(lg), None, C.byref(out), ws, n.value - 1,
+                           None, None) == 6
+    assert lib.moe_forward(h, C.byref(x), C.byref(lg), None, C.byref(out), C.c_void_p(0x10010),
+                           n.value, None, None) == 6          # misaligned
+    # T = 0: nothing to do, no launch
+    x0, lg0, o0 = _t(L, [0, 64], BF), _t(L, [0, 8], F32), _t(L, [0, 64], BF)
+    assert lib.moe_forward(h, C.byref(x0), C.byref(lg0), None, C.byref(o0), None, 0,
+                           None, None) == 0
+    lib.moe_destroy(h)
+
+
+def test_workspace_grows_with_tokens(L):
+    st, h = create(L)
+    a, b = C.c_size_t(), C.c_size_t()
+    L.lib().moe_workspace_size(h, 10, C.byref(a))
+    L.lib().moe_workspace_size(h, 1000, C.byref(b))
+    assert b.value > a.value
+    assert L.lib().moe_destroy(h) == 0
+    assert L.lib().moe_destroy(None) == 0

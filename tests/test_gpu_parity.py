@@ -1,0 +1,212 @@
+"""GPU parity of the HIP layer against the fp64 CPU oracle, through the C ABI.
+
+Bar (from the layer's acceptance criteria): routing ids, per-expert counts and
+the permutation bit-exact; max |err| <= 1e-4 * RMS(out) for f32 layers and
+<= 2e-2 * RMS(out) for bf16 / MXFP4 layers, the oracle fed the identical
+bf16 / MXFP4 inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_ffn_03_amd import synth
+from parity_util import (check_routing, compare_out, host, host_experts, run_gpu,
+                         sample_tokens)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def oracle_full(cfg, inp, T=None):
+    return oracle.forward(oracle.params_of(cfg, T=T), host(inp))
+
+
+# ------------------------------------------------------------------ small sizes
+
+@pytest.mark.parametrize("name", synth.SMALL_CONFIGS)
+@pytest.mark.parametrize("variant", [0, 1, 2])
+def test_small_configs_elementwise(name, variant):
+    """Every output element of the five workloads at oracle-sized shapes, with
+    the kernel choice automatic, forced large-M, and forced small-M."""
+    cfg = synth.CONFIGS[name]
+    if cfg.w_dtype == "f32" and variant:
+        pytest.skip("f32 layers have one kernel")
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, _ = run_gpu(cfg, inp, gemm_variant=variant)
+    check_routing(cfg, inp, r, cfg.T)
+    ref = oracle_full(cfg, inp)
+    compare_out(out, ref["out"], cfg.x_dtype, f"{name} variant {variant}")
+
+
+@pytest.mark.parametrize("layout", ["split", "interleaved", "unfused"])
+@pytest.mark.parametrize("w_dtype", ["bf16", "mxfp4", "f32"])
+@pytest.mark.parametrize("variant", [1, 2])
+def test_layouts_dtypes_biases(layout, w_dtype, variant):
+    """Each gate||up layout with each weight type, expert biases on, ragged
+    token count and feature tails."""
+    x_dtype = "f32" if w_dtype == "f32" else "bf16"
+    if w_dtype == "f32" and variant == 2:
+        pytest.skip("f32 layers have one kernel")
+    cfg = synth.MoeConfig(name="lay", cid=201, T=333, H=352, I=224, E=6, K=2,
+                          x_dtype=x_dtype, w_dtype=w_dtype, layout=layout,
+                          expert_biases=True, bias_std=0.5, renormalize=True)
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, _ = run_gpu(cfg, inp, gemm_variant=variant)
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], x_dtype,
+                f"{layout}/{w_dtype}/variant {variant}")
+
+
+@pytest.mark.parametrize("act", [("silu", 1.0, 0.0, 0.0), ("swiglu_clamped", 1.702, 1.0, 7.0),
+                                 ("swiglu_clamped", 1.0, 0.0, 0.0),
+                                 ("swiglu_clamped", 0.5, -0.25, 1.5)])
+def test_activations(act):
+    name, a, b, lim = act
+    cfg = synth.MoeConfig(name="act", cid=202, T=200, H=256, I=192, E=4, K=2,
+                          activation=name, swiglu_alpha=a, swiglu_beta=b,
+                          swiglu_limit=lim, expert_biases=True, bias_std=1.0)
+    inp = synth.make_inputs(cfg, device=DEV)
+    inp["x"] = (inp["x"].float() * 3).to(torch.bfloat16)   # drive the clamp
+    out, r, _ = run_gpu(cfg, inp)
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"activation {act}")
+
+
+@pytest.mark.parametrize("routing", [
+    dict(scoring="softmax", renormalize=False),
+    dict(scoring="softmax", renormalize=True, routed_scaling_factor=2.5),
+    dict(scoring="sigmoid", renormalize=False),
+    dict(scoring="sigmoid", renormalize=True, selection_bias_std=0.1),
+    dict(scoring="softmax", renormalize=False, selection_bias_std=0.05),
+    dict(scoring="sigmoid", renormalize=True, selection_bias_std=0.1, n_group=8,
+         topk_group=3, routed_scaling_factor=1.5),
+    dict(scoring="softmax", renormalize=True, n_group=4, topk_group=2),
+])
+def test_routing_modes(routing):
+    cfg = synth.MoeConfig(name="rt", cid=203, T=700, H=128, I=64, E=64, K=6, **routing)
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, _ = run_gpu(cfg, inp)
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"routing {routing}")
+
+
+# ------------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("T", [1, 2, 63, 257])
+def test_ragged_token_counts(T):
+    cfg = synth.MIXTRAL_SMALL.replace(T=T)
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, _ = run_gpu(cfg, inp)
+    check_routing(cfg, inp, r, T)
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"T={T}")
+
+
+def test_zero_tokens():
+    cfg = synth.MIXTRAL_SMALL.replace(T=0)
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, _ = run_gpu(cfg, inp)
+    assert out.shape == (0, cfg.H)
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+def test_all_tokens_on_one_expert(variant):
+    """A fully skewed load: one expert holds every token's first slot, many
+    experts are empty (zero-row experts launch no tiles)."""
+    cfg = synth.MoeConfig(name="skew", cid=204, T=900, H=192, I=160, E=16, K=2)
+    inp = synth.make_inputs(cfg, device=DEV)
+    inp["logits"][:, 5] += 20.0
+    inp["logits"][:, 11] += 10.0
+    out, r, _ = run_gpu(cfg, inp, gemm_variant=variant)
+    counts = r["expert_counts"].cpu().numpy()
+    assert counts[5] == cfg.T and counts[11] == cfg.T
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"skew variant {variant}")
+
+
+@pytest.mark.parametrize("E,K", [(1, 1), (6, 6), (6, 1), (130, 7), (256, 64)])
+def test_expert_counts(E, K):
+    cfg = synth.MoeConfig(name="ek", cid=205, T=150, H=64, I=96, E=E, K=K)
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, _ = run_gpu(cfg, inp)
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"E={E} K={K}")
+
+
+def test_ties_and_equal_logits():
+    """Equal logits everywhere: ids 0..K-1 on every token (lower index wins)."""
+    cfg = synth.MoeConfig(name="tie", cid=206, T=40, H=64, I=64, E=16, K=4)
+    inp = synth.make_inputs(cfg, device=DEV)
+    inp["logits"].zero_()
+    out, r, _ = run_gpu(cfg, inp)
+    assert (r["topk_ids"].cpu() == torch.arange(4, dtype=torch.int32)).all()
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", "ties")
+
+
+def test_shared_output_and_3d_input():
+    """The shared-expert output folds into the combine (QMoEWoQ::forward);
+    a [B, S, H] input is a flat [B*S, H] batch (ONNX MoE input)."""
+    cfg = synth.MoeConfig(name="sh", cid=207, T=96, H=128, I=64, E=8, K=2,
+                          shared_output=True)
+    inp = synth.make_inputs(cfg, device=DEV)
+    ref = oracle_full(cfg, inp)["out"]
+    inp3 = dict(inp)
+    inp3["x"] = inp["x"].view(4, 24, cfg.H)
+    inp3["shared_output"] = inp["shared_output"].view(4, 24, cfg.H)
+    out, _, _ = run_gpu(cfg, inp3, routing=False)
+    assert out.shape == (4, 24, cfg.H)
+    compare_out(out.view(96, cfg.H), ref, "bf16", "shared + 3-D")
+
+
+def test_deterministic():
+    """No value atomics: two runs give bitwise-identical outputs and routing."""
+    cfg = synth.DEEPSEEK_SMALL
+    inp = synth.make_inputs(cfg, device=DEV)
+    a, ra, layer = run_gpu(cfg, inp)
+    b = layer(inp["x"], inp["logits"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_forward_errors_on_device():
+    from mixture_experts_ffn_03_amd import _lib
+    cfg = synth.MIXTRAL_SMALL.replace(T=8)
+    inp = synth.make_inputs(cfg, device=DEV)
+    _, _, layer = run_gpu(cfg, inp)
+    with pytest.raises(_lib.MoeError) as ei:
+        layer(inp["x"].float(), inp["logits"])
+    assert ei.value.status == 5
+    with pytest.raises(_lib.MoeError) as ei:
+        layer(inp["x"], inp["logits"][:, :4].contiguous())
+    assert ei.value.status == 2
+
+
+# ------------------------------------------------------------------ full sizes
+
+@pytest.mark.parametrize("name", synth.FULL_CONFIGS)
+def test_full_size_routing(name):
+    """Routing and permutation of every token at the measured shapes."""
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg, device=DEV)
+    layer_inp = inp
+    out, r, _ = run_gpu(cfg, layer_inp)
+    check_routing(cfg, inp, r, cfg.T)
+
+
+@pytest.mark.parametrize("name,n", [("mixtral_prefill", 24), ("qwen3_decode", 32),
+                                    ("gptoss_mxfp4", 48), ("deepseek_v3", 16),
+                                    ("tiny_fp32", 16)])
+def test_full_size_sampled(name, n):
+    """At the measured shapes (the kernels the benchmark times), every element
+    of a sample of tokens against the oracle run on exactly those tokens."""
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, _ = run_gpu(cfg, inp)
+    ro = check_routing(cfg, inp, r, cfg.T)
+    toks = sample_tokens(cfg.T, n)
+    hin = host_experts(inp, np.unique(ro["ids"][toks]))
+    ref = oracle.forward(oracle.params_of(cfg), hin, tokens=toks)
+    assert (ref["ids"] == ro["ids"][toks]).all()
+    compare_out(out[torch.as_tensor(toks, device=out.device)], ref["out"], cfg.x_dtype,
+                f"{name} full size, {len(toks)} tokens")
