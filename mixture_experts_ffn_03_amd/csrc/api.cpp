@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -23,6 +24,11 @@ struct moe_layer {
     moe_options opts;
     moe_weights w;
     bool bound;
+    // Prepared state (QMoEWoQ "pack once, thread-safe"): whether the down
+    // weights convert exactly to fp16, which enables the fp16 down GEMM.
+    mutable std::mutex mu;
+    mutable bool prepared;
+    mutable int down_f16_ok;
 };
 
 namespace {
@@ -114,8 +120,14 @@ size_t align256(size_t v)
 // Workspace carving.  Every region starts on a 256-byte boundary.
 struct Workspace {
     size_t ids, weights, block_counts, block_base, counts, offsets, tile_cum1, tile_cum2,
-        row_token, slot_row, h, y, total;
+        row_token, slot_row, hfmt, h, y, total;
 };
+
+int64_t max_m_tiles_of(const moe_layer *l, int64_t T, int bm)
+{
+    const int64_t TK = T * l->K;
+    return (TK + bm - 1) / bm + (l->E < TK ? l->E : TK);
+}
 
 Workspace layout(const moe_layer *l, int64_t T)
 {
@@ -139,6 +151,15 @@ Workspace layout(const moe_layer *l, int64_t T)
     w.tile_cum2 = take((l->E + 1) * 4);
     w.row_token = take(TK * 4);
     w.slot_row = take(TK * 4);
+    // one h-format byte per (GEMM-1 M-tile, GEMM-1 feature tile), worst case
+    // over the two 16-bit kernel variants
+    size_t nfmt = 0;
+    for (GemmKind k : {GemmKind::kPrefill, GemmKind::kDecode}) {
+        const int64_t ntile = (l->I + gemm_bn(k, true) - 1) / gemm_bn(k, true);
+        const size_t n = (size_t)(max_m_tiles_of(l, T, gemm_bm(k)) * ntile);
+        if (n > nfmt) nfmt = n;
+    }
+    w.hfmt = take(nfmt);
     w.h = take(TK * l->I * hbytes);
     w.y = take(TK * l->H * 4);
     w.total = o;
@@ -276,6 +297,37 @@ moe_status check_workspace(const moe_layer *l, int64_t T, void *ws, size_t bytes
     return MOE_OK;
 }
 
+// Prepare once per binding: scan the down-weight range on `s` and decide
+// whether the down GEMM may run in fp16 (bf16 magnitudes <= 65280, or MXFP4
+// scale bytes in [104, 140], convert exactly).  Synchronises `s` once.
+moe_status prepare_locked(const moe_layer *l, hipStream_t s)
+{
+    std::lock_guard<std::mutex> lock(l->mu);
+    if (l->prepared) return MOE_OK;
+    int ok = 0;
+    if (l->wdtype != MOE_DTYPE_F32) {
+        uint32_t *d = nullptr;
+        moe_status st = hip_check(hipMalloc((void **)&d, 16), "prepare alloc");
+        if (st) return st;
+        const uint32_t init[4] = {0u, 255u, 0u, 0u};
+        const bool mx = l->wdtype == MOE_DTYPE_MXFP4;
+        const int64_t elems = l->E * l->H * l->I;
+        uint32_t r[4] = {0, 0, 0, 0};
+        hipError_t e = hipMemcpyAsync(d, init, sizeof init, hipMemcpyHostToDevice, s);
+        if (e == hipSuccess)
+            e = launch_weight_range(l->w.down_experts.data, l->w.down_experts.scales,
+                                    mx ? 0 : elems / 2, mx ? elems / 32 : 0, d, s);
+        if (e == hipSuccess) e = hipMemcpyAsync(r, d, sizeof r, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        (void)hipFree(d);
+        if ((st = hip_check(e, "prepare weight scan"))) return st;
+        ok = mx ? (r[1] >= 104u && r[2] <= 140u) : (r[0] <= 0x477fu);
+    }
+    l->down_f16_ok = ok;
+    l->prepared = true;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -354,6 +406,8 @@ moe_status moe_create(int64_t E, int64_t H, int64_t I, int64_t K, moe_dtype wdty
     l->has_d_bias = has_d_bias ? 1 : 0;
     l->opts = o;
     l->bound = false;
+    l->prepared = false;
+    l->down_f16_ok = 0;
     *out = l;
     return MOE_OK;
 }
@@ -400,16 +454,19 @@ moe_status moe_set_weights(moe_layer *l, const moe_weights *w)
         (st = check_tensor("e_score_correction_bias", w->e_score_correction_bias,
                            MOE_DTYPE_F32, {E})))
         return st;
+    std::lock_guard<std::mutex> lock(l->mu);
     l->w = *w;
     l->bound = true;
+    l->prepared = false;   // re-binding drops the prepared state
     return MOE_OK;
 }
 
 moe_status moe_prepare(moe_layer *l, void *stream)
 {
-    (void)stream;
     if (!l) return fail(MOE_ERR_INVALID_ARGUMENT, "layer is NULL");
-    return check_bound(l);
+    moe_status st = check_bound(l);
+    if (st) return st;
+    return prepare_locked(l, (hipStream_t)stream);
 }
 
 moe_status moe_workspace_size(const moe_layer *l, int64_t T, size_t *bytes)
@@ -488,6 +545,7 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     if ((st = check_workspace(l, T, ws, ws_bytes, &W))) return st;
 
     hipStream_t s = (hipStream_t)stream;
+    if ((st = prepare_locked(l, s))) return st;
     char *wsb = (char *)ws;
     auto mark = [&](int i) -> moe_status {
         if (events && events[i])
@@ -498,9 +556,8 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     if ((st = mark(0))) return st;
     if ((st = run_route(l, (const float *)logits->data, T, wsb, W, path, s, events))) return st;
 
-    const int64_t TK = T * l->K;
     const int bm = path_bm(path);
-    const int64_t max_m_tiles = (TK + bm - 1) / bm + (l->E < TK ? l->E : TK);
+    const int64_t max_m_tiles = max_m_tiles_of(l, T, bm);
     const bool mx = l->wdtype == MOE_DTYPE_MXFP4;
     const bool fz = fused(l);
 
@@ -521,6 +578,10 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     g1.alpha = l->opts.swiglu_alpha;
     g1.beta = l->opts.swiglu_beta;
     g1.limit = l->opts.swiglu_limit;
+    g1.hfmt = (uint8_t *)(wsb + W.hfmt);
+    g1.h_tiles = g1.nN;
+    g1.h_width = bn1;
+    g1.f16_ok = l->down_f16_ok;
     WeightRows &w1 = g1.w;
     if (fz) {
         w1.w_gate = w1.w_up = l->w.gate_up_experts.data;
@@ -566,6 +627,10 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     g2.w.e_rows = l->H;
     g2.w.row_mul = 1;
     if (present(l->w.down_bias)) g2.w.b_gate = l->w.down_bias.data;
+    g2.hfmt = g1.hfmt;
+    g2.h_tiles = g1.nN;
+    g2.h_width = bn1;
+    g2.f16_ok = g1.f16_ok;
 
     if (max_m_tiles * (g1.nN > g2.nN ? g1.nN : g2.nN) + 8 > 0x7fffffffLL)
         return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch");

@@ -1,29 +1,35 @@
-// Grouped expert GEMMs on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16).
+// Grouped expert GEMMs on gfx950 MFMA (v_mfma_f32_32x32x16_{bf16,f16}).
 //
 // Each workgroup computes one tile of Y^T = W_e * A^T for one expert e:
 // BN weight rows (output features) by BM permutation rows (tokens), fp32
 // accumulation, reduction in BK-wide steps through double-buffered LDS.
 // The weight panel is the MFMA "A" operand and the token panel the "B"
 // operand, so each lane ends with four consecutive output features of one
-// token -- 8-byte bf16 / 16-byte f32 stores in the epilogue.
+// token -- 8-byte 16-bit / 16-byte f32 stores in the epilogue.
 //
 // Two epilogues:
 //  gated  (gate||up GEMM, ONNX "MoE" fc1/fc3): the BN weight rows of a tile
 //         are BN/2 gate rows and the BN/2 up rows of the same features; a
 //         wave holds the gate and up accumulators of the same features in
-//         the same lanes, adds the biases, applies the gated activation and
-//         stores h in bf16 (the MFMA operand of the next GEMM).
-//  down   (ONNX "MoE" fc2): adds the down bias and stores y in f32; the
-//         combine rounds once, after the weighted sum.
+//         the same lanes, adds the biases and applies the gated activation.
+//         h is stored in fp16 (11-bit significand, 8x finer than bf16) when
+//         the whole tile fits fp16's range and the down weights convert
+//         exactly, else in bf16; one format byte per tile records the choice.
+//  down   (ONNX "MoE" fc2): when every h tile of its rows is fp16 (the
+//         normal case), a workgroup converts the bf16 (or MXFP4) down weights
+//         exactly to fp16 on their way into LDS and runs the f16 MFMA;
+//         otherwise it rounds the fp16 h tiles to bf16 and runs the bf16 MFMA.
+//         Adds the down bias and stores y in f32; the combine rounds once,
+//         after the weighted sum.
 //
 // The A operand of the gated GEMM is gathered straight from x through the
 // permutation (row_token), so the permuted activations are never written.
 //
 // MXFP4 weights ("ClikaRT::nn::QMoEWoQ": decode one block at a time inside
 // the GEMM dot, never a dense copy): each 16-byte code chunk is one 32-element
-// block; it is decoded with its e8m0 scale to bf16 by the gfx950 scaled
-// conversion (exact: e2m1 times a power of two fits bf16) on its way into
-// LDS, and the MFMA stays bf16 x bf16 (weight-only; the activation is not
+// block; it is decoded with its e8m0 scale by the gfx950 scaled conversion
+// (exact: e2m1 times a power of two fits the 16-bit format) on its way into
+// LDS, and the MFMA stays 16-bit x 16-bit (weight-only; the activation is not
 // quantised).
 #include "gemm_common.h"
 
@@ -33,6 +39,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -44,7 +54,7 @@ struct Tile {
     static constexpr int TN = BN / WN, TM = BM / WM; // wave tile
     static constexpr int FN = TN / 32, FM = TM / 32; // 32x32 MFMA blocks per wave
     static constexpr int LDK = BK + 8;               // padded LDS row (elements)
-    static constexpr int CPR = BK / 8;               // 16-byte bf16 chunks per row
+    static constexpr int CPR = BK / 8;               // 16-byte 16-bit chunks per row
     static constexpr int QPR = BK / 32;              // 16-byte MXFP4 chunks per row
     static constexpr int A_CH = BM * CPR / NT;
     static constexpr int B_CH_BF16 = BN * CPR / NT;
@@ -54,7 +64,7 @@ struct Tile {
     static_assert(B_CH_BF16 * NT == BN * CPR, "B tile chunks");
     static_assert(B_CH_MX * NT == BN * QPR, "MXFP4 tile chunks");
     static_assert(FN >= 2 && FN % 2 == 0, "gate/up pairs per wave");
-    static_assert(2 * STAGE * 2 + (kMaxExperts + 1) * 4 <= 160 * 1024, "LDS");
+    static_assert(2 * STAGE * 2 + (kMaxExperts + 1) * 4 + 64 <= 160 * 1024, "LDS");
 };
 
 using PrefillTile = Tile<256, 256, 64, 4, 2>;   // 512 threads, wave 64x128
@@ -73,22 +83,71 @@ __device__ inline float e8m0_scale(uint32_t x)
     return __uint_as_float(x << 23);
 }
 
-template <class TL, bool MX, bool GATED>
-__global__ __launch_bounds__(TL::NT) void gemm_kernel(GemmArgs g)
+// Two bf16 (low, high half of w) -> two fp16, exact for values in fp16's
+// normal range (the prepare-time range check guarantees it).
+__device__ inline uint32_t bf16x2_to_f16x2(uint32_t w)
+{
+    const fp16x2 p = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16),
+                                                __uint_as_float(w & 0xffff0000u));
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// Two fp16 -> two bf16, round to nearest even.
+__device__ inline uint32_t f16x2_to_bf16x2(uint32_t w)
+{
+    const f16x2 h = __builtin_bit_cast(f16x2, w);
+    const bf16x2 b = {(__bf16)(float)h[0], (__bf16)(float)h[1]};
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+// 32 MXFP4 elements (16 code bytes, element 2i in the low nibble of byte i)
+// times 2^(X-127) -> 32 16-bit values (bf16 or fp16) in `dst` (16-byte aligned).
+template <bool F16>
+__device__ inline void decode_mxfp4(const u32x4 &codes, float sc, uint16_t *dst)
+{
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t word = codes[w];
+        u32x4 o;
+        if (F16) {
+            o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc, 0));
+            o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc, 1));
+            o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc, 2));
+            o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc, 3));
+        } else {
+            o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0));
+            o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1));
+            o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2));
+            o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3));
+        }
+        *(u32x4 *)(dst + w * 8) = o;
+    }
+}
+
+template <bool F16>
+__device__ inline f32x16 mfma(const u32x4 &a, const u32x4 &b, const f32x16 &c)
+{
+    if (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// One tile.  F16: operands of the MFMA are fp16 (down GEMM whose h tiles are
+// all fp16); otherwise bf16.
+template <class TL, bool MX, bool GATED, bool F16>
+__device__ __forceinline__ void gemm_body(const GemmArgs &g, const TileWork &tw,
+                                          uint16_t *lds, float *s_red)
 {
     constexpr int B_CH = MX ? TL::B_CH_MX : TL::B_CH_BF16;
-    constexpr int NW = GATED ? TL::BN / 2 : TL::BN;   // output features per tile
-    __shared__ __attribute__((aligned(16))) __bf16 lds[2 * TL::STAGE];
-    __shared__ int s_cum[kMaxExperts + 1];
-
-    TileWork tw;
-    if (!find_tile(g, s_cum, TL::BM, NW, &tw)) return;
+    constexpr int NWAVES = TL::NT / 64;
     const int tid = threadIdx.x;
     const int Kd = g.Kd;
 
     // ---- A (token) rows: gathered through the permutation when row_token is set
     const int a_kc = (tid % TL::CPR) * 8;
-    const __bf16 *a_ptr[TL::A_CH];
+    const uint16_t *a_ptr[TL::A_CH];
     int a_lr[TL::A_CH];
 #pragma unroll
     for (int i = 0; i < TL::A_CH; ++i) {
@@ -96,7 +155,7 @@ __global__ __launch_bounds__(TL::NT) void gemm_kernel(GemmArgs g)
         const int r = tw.row0 + min(lr, tw.nrows - 1);
         const int src = g.row_token ? g.row_token[r] : r;
         a_lr[i] = lr;
-        a_ptr[i] = (const __bf16 *)g.a + (int64_t)src * Kd + a_kc;
+        a_ptr[i] = (const uint16_t *)g.a + (int64_t)src * Kd + a_kc;
     }
 
     // ---- B (weight) rows
@@ -123,6 +182,13 @@ __global__ __launch_bounds__(TL::NT) void gemm_kernel(GemmArgs g)
         }
     }
 
+    // h formats of this tile's rows (bf16 down GEMM): an fp16 h step is
+    // rounded to bf16 on its way into LDS
+    const uint8_t *hf = GATED ? nullptr : g.hfmt + (int64_t)tw.mg * g.h_tiles;
+    auto a_is_f16 = [&](int kt) -> bool {
+        return !GATED && !F16 && hf[(kt * TL::BK) / g.h_width] == kHF16;
+    };
+
     u32x4 ra[TL::A_CH], rb[B_CH];
     uint32_t rs[B_CH];
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -144,29 +210,29 @@ __global__ __launch_bounds__(TL::NT) void gemm_kernel(GemmArgs g)
         }
     };
 
-    auto lstore = [&](int st) {
-        __bf16 *la = lds + st * TL::STAGE;
-        __bf16 *lb = la + TL::BM * TL::LDK;
+    auto lstore = [&](int st, bool a_f16) {
+        uint16_t *la = lds + st * TL::STAGE;
+        uint16_t *lb = la + TL::BM * TL::LDK;
 #pragma unroll
-        for (int i = 0; i < TL::A_CH; ++i)
-            *(u32x4 *)(la + a_lr[i] * TL::LDK + a_kc) = ra[i];
+        for (int i = 0; i < TL::A_CH; ++i) {
+            u32x4 v = ra[i];
+            if (a_f16) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) v[w] = f16x2_to_bf16x2(v[w]);
+            }
+            *(u32x4 *)(la + a_lr[i] * TL::LDK + a_kc) = v;
+        }
 #pragma unroll
         for (int i = 0; i < B_CH; ++i) {
             if (MX) {
-                const float sc = e8m0_scale(rs[i]);
-                __bf16 *dst = lb + b_lr[i] * TL::LDK + b_kc * 32;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t word = rb[i][w];
-                    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0);
-                    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1);
-                    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2);
-                    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3);
-                    bf16x8 o = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-                    *(bf16x8 *)(dst + w * 8) = o;
-                }
+                decode_mxfp4<F16>(rb[i], e8m0_scale(rs[i]), lb + b_lr[i] * TL::LDK + b_kc * 32);
             } else {
-                *(u32x4 *)(lb + b_lr[i] * TL::LDK + b_kc * 8) = rb[i];
+                u32x4 v = rb[i];
+                if (F16) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) v[w] = bf16x2_to_f16x2(v[w]);
+                }
+                *(u32x4 *)(lb + b_lr[i] * TL::LDK + b_kc * 8) = v;
             }
         }
     };
@@ -191,66 +257,105 @@ __global__ __launch_bounds__(TL::NT) void gemm_kernel(GemmArgs g)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[f][m][r] = 0.0f;
 
-    const int nk = (Kd + TL::BK - 1) / TL::BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        const __bf16 *la = lds + cur * TL::STAGE;
-        const __bf16 *lb = la + TL::BM * TL::LDK;
+    auto compute = [&](int st) {
+        const uint16_t *la = lds + st * TL::STAGE;
+        const uint16_t *lb = la + TL::BM * TL::LDK;
 #pragma unroll
         for (int ks = 0; ks < TL::BK / 16; ++ks) {
-            bf16x8 bf[TL::FN], af[TL::FM];
+            u32x4 bf[TL::FN], af[TL::FM];
 #pragma unroll
             for (int f = 0; f < TL::FN; ++f)
-                bf[f] = *(const bf16x8 *)(lb + (brow(f) + lrow) * TL::LDK + ks * 16 + lk);
+                bf[f] = *(const u32x4 *)(lb + (brow(f) + lrow) * TL::LDK + ks * 16 + lk);
 #pragma unroll
             for (int m = 0; m < TL::FM; ++m)
-                af[m] = *(const bf16x8 *)(la + (wm * TL::TM + m * 32 + lrow) * TL::LDK +
-                                          ks * 16 + lk);
+                af[m] = *(const u32x4 *)(la + (wm * TL::TM + m * 32 + lrow) * TL::LDK +
+                                         ks * 16 + lk);
 #pragma unroll
             for (int f = 0; f < TL::FN; ++f)
 #pragma unroll
                 for (int m = 0; m < TL::FM; ++m)
-                    acc[f][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[f], af[m],
-                                                                        acc[f][m], 0, 0, 0);
+                    acc[f][m] = mfma<F16>(bf[f], af[m], acc[f][m]);
         }
-        if (kt + 1 < nk) lstore(cur ^ 1);
+    };
+
+    const int nk = (Kd + TL::BK - 1) / TL::BK;
+    gload(0);
+    lstore(0, a_is_f16(0));
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) gload(kt + 1);
+        compute(cur);
+        if (more) lstore(cur ^ 1, a_is_f16(kt + 1));
         __syncthreads();
     }
 
     // ---- epilogue: lane holds features 8*i4 + 4*(lane/32) + j of token lane%32
     const int fq = (lane >> 5) * 4;
     if (GATED) {
-        __bf16 *h = (__bf16 *)g.out;
+        // pass 1: activation into the gate accumulators, tile max |h|
         const int64_t eb = (int64_t)tw.e * g.w.e_rows;
+        float hmax = 0.0f;
+#pragma unroll
+        for (int fp = 0; fp < TL::FN / 2; ++fp)
+#pragma unroll
+            for (int m = 0; m < TL::FM; ++m) {
+                const bool tok_ok = wm * TL::TM + m * 32 + lrow < tw.nrows;
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int c = tw.n0 + wn * (TL::TN / 2) + fp * 32 + i4 * 8 + fq;
+                    const bool ok = tok_ok && c < g.Nout;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float gv = acc[fp][m][i4 * 4 + j];
+                        float uv = acc[fp + TL::FN / 2][m][i4 * 4 + j];
+                        if (ok && g.w.b_gate)
+                            gv += bias_at(g.w.b_gate,
+                                          eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_gate);
+                        if (ok && g.w.b_up)
+                            uv += bias_at(g.w.b_up,
+                                          eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_up);
+                        const float h = gated_act(g.act, gv, uv, g.alpha, g.beta, g.limit);
+                        acc[fp][m][i4 * 4 + j] = h;
+                        if (ok) hmax = fmaxf(hmax, fabsf(h));
+                    }
+                }
+            }
+        // block max -> storage format of this h tile
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, off, 64));
+        if (lane == 0) s_red[wave] = hmax;
+        __syncthreads();
+        float bmax = s_red[0];
+#pragma unroll
+        for (int w = 1; w < NWAVES; ++w) bmax = fmaxf(bmax, s_red[w]);
+        const bool f16 = g.f16_ok && bmax <= 65504.0f;
+        if (tid == 0) g.hfmt[(int64_t)tw.mg * g.h_tiles + tw.nt] = f16 ? kHF16 : kHBF16;
+        // pass 2: store h
+        uint16_t *h = (uint16_t *)g.out;
 #pragma unroll
         for (int fp = 0; fp < TL::FN / 2; ++fp)
 #pragma unroll
             for (int m = 0; m < TL::FM; ++m) {
                 const int tl = wm * TL::TM + m * 32 + lrow;
                 if (tl >= tw.nrows) continue;
-                __bf16 *hrow = h + (int64_t)(tw.row0 + tl) * g.Nout;
+                uint16_t *hrow = h + (int64_t)(tw.row0 + tl) * g.Nout;
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
                     const int c = tw.n0 + wn * (TL::TN / 2) + fp * 32 + i4 * 8 + fq;
                     if (c >= g.Nout) continue;
-                    bf16x4 o;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float gv = acc[fp][m][i4 * 4 + j];
-                        float uv = acc[fp + TL::FN / 2][m][i4 * 4 + j];
-                        if (g.w.b_gate)
-                            gv += bias_at(g.w.b_gate,
-                                          eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_gate);
-                        if (g.w.b_up)
-                            uv += bias_at(g.w.b_up,
-                                          eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_up);
-                        o[j] = (__bf16)gated_act(g.act, gv, uv, g.alpha, g.beta, g.limit);
+                    const f32x16 &a = acc[fp][m];
+                    const int r0 = i4 * 4;
+                    if (f16) {
+                        f16x4 o = {(_Float16)a[r0], (_Float16)a[r0 + 1], (_Float16)a[r0 + 2],
+                                   (_Float16)a[r0 + 3]};
+                        *(f16x4 *)(hrow + c) = o;
+                    } else {
+                        bf16x4 o = {(__bf16)a[r0], (__bf16)a[r0 + 1], (__bf16)a[r0 + 2],
+                                    (__bf16)a[r0 + 3]};
+                        *(bf16x4 *)(hrow + c) = o;
                     }
-                    *(bf16x4 *)(hrow + c) = o;
                 }
             }
     } else {
@@ -281,11 +386,62 @@ __global__ __launch_bounds__(TL::NT) void gemm_kernel(GemmArgs g)
 }
 
 template <class TL, bool MX, bool GATED>
+__global__ __launch_bounds__(TL::NT) void gemm_kernel(GemmArgs g)
+{
+    constexpr int NW = GATED ? TL::BN / 2 : TL::BN;   // output features per tile
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * TL::STAGE];
+    __shared__ int s_cum[kMaxExperts + 1];
+    __shared__ float s_red[TL::NT / 64];
+
+    TileWork tw;
+    if (!find_tile(g, s_cum, TL::BM, NW, &tw)) return;
+    if (GATED) {
+        gemm_body<TL, MX, GATED, false>(g, tw, lds, s_red);
+        return;
+    }
+    // down GEMM: fp16 operands iff every h tile of these rows is fp16
+    const uint8_t *hf = g.hfmt + (int64_t)tw.mg * g.h_tiles;
+    int all16 = g.f16_ok;
+    for (int i = threadIdx.x; i < g.h_tiles; i += TL::NT) all16 &= hf[i] == kHF16;
+    if (__syncthreads_and(all16)) gemm_body<TL, MX, GATED, true>(g, tw, lds, s_red);
+    else gemm_body<TL, MX, GATED, false>(g, tw, lds, s_red);
+}
+
+template <class TL, bool MX, bool GATED>
 hipError_t launch(const GemmArgs &a, int64_t max_m_tiles, hipStream_t s)
 {
     const int64_t grid = max_m_tiles * a.nN + 8;
     gemm_kernel<TL, MX, GATED><<<dim3((unsigned)grid), dim3(TL::NT), 0, s>>>(a);
     return hipGetLastError();
+}
+
+// ---- prepare-time range scan of a down-weight stack
+__global__ __launch_bounds__(256) void weight_range_kernel(const uint32_t *w, const uint8_t *sc,
+                                                           int64_t n_words, int64_t n_scales,
+                                                           uint32_t *out)
+{
+    uint32_t mx = 0, smin = 255, smax = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += stride) {
+        const uint32_t v = w[i];
+        mx = max(mx, max(v & 0x7fffu, (v >> 16) & 0x7fffu));
+    }
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_scales; i += stride) {
+        const uint32_t b = sc[i];
+        smin = min(smin, b);
+        smax = max(smax, b);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+        smin = min(smin, (uint32_t)__shfl_xor((int)smin, off, 64));
+        smax = max(smax, (uint32_t)__shfl_xor((int)smax, off, 64));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        atomicMax(&out[0], mx);
+        atomicMin(&out[1], smin);
+        atomicMax(&out[2], smax);
+    }
 }
 
 }  // namespace
@@ -316,6 +472,14 @@ hipError_t launch_gemm_bf16(GemmKind kind, bool gated, bool mxfp4, const GemmArg
                      : launch<DecodeTile, true, false>(a, max_m_tiles, s);
     return gated ? launch<DecodeTile, false, true>(a, max_m_tiles, s)
                  : launch<DecodeTile, false, false>(a, max_m_tiles, s);
+}
+
+hipError_t launch_weight_range(const void *w, const uint8_t *scales, int64_t n_words,
+                               int64_t n_scales, uint32_t *out, hipStream_t s)
+{
+    weight_range_kernel<<<1024, 256, 0, s>>>((const uint32_t *)w, scales, n_words, n_scales,
+                                             out);
+    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -10,6 +10,8 @@ namespace moe {
 // permutation, output features [n0, n0 + tile width).
 struct TileWork {
     int e, row0, nrows, n0;
+    int mg;      // global M-tile index (tile_cum[e] + token tile)
+    int nt;      // feature tile index
 };
 
 // Map this workgroup to a tile, or return false when it has none.
@@ -46,6 +48,8 @@ __device__ inline bool find_tile(const GemmArgs &g, int *s_cum, int bm, int n_wi
     w->row0 = g.offsets[e] + mtile * bm;
     w->nrows = min(bm, g.counts[e] - mtile * bm);
     w->n0 = nt * n_width;
+    w->mg = s_cum[e] + mtile;
+    w->nt = nt;
     return true;
 }
 

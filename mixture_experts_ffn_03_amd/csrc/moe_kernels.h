@@ -54,6 +54,9 @@ struct WeightRows {
     const void *b_up;
 };
 
+// Storage format of one h tile (GEMM-1 output tile, read by the down GEMM).
+enum : uint8_t { kHF16 = 0, kHBF16 = 1 };
+
 struct GemmArgs {
     const void *a;               // activations: x [T, Kd] or h [T*K, Kd]
     const int32_t *row_token;    // if set, A row r reads a[row_token[r]]
@@ -68,7 +71,19 @@ struct GemmArgs {
     void *out;                   // h bf16 [T*K, I] or y f32 [T*K, H]
     int act;                     // 0 SiLU-gated, 1 clamped SwiGLU
     float alpha, beta, limit;
+    // h storage formats, one byte per (GEMM-1 M-tile, GEMM-1 feature tile):
+    // written by the gated GEMM, read per reduction step by the down GEMM.
+    uint8_t *hfmt;
+    int h_tiles;                 // GEMM-1 feature tiles (row stride of hfmt)
+    int h_width;                 // h columns per GEMM-1 feature tile
+    int f16_ok;                  // the down weights convert exactly to fp16
 };
+
+// Range of a down-weight stack, for the choice of the fp16 down GEMM:
+// out[0] = max over elements of the bf16 magnitude bits (0x7f80 = inf),
+// out[1] = min MXFP4 scale byte, out[2] = max MXFP4 scale byte.
+hipError_t launch_weight_range(const void *w, const uint8_t *scales, int64_t n_words,
+                               int64_t n_scales, uint32_t *out, hipStream_t s);
 
 struct CombineArgs {
     const float *y;              // [T*K, H] (row order of the permutation)

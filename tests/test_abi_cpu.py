@@ -2,7 +2,9 @@
 
 The library must load, export every function include/moe_mi355x.h declares,
 and reject bad declarations / bindings / calls with the documented status
-codes before touching the device (clika "ClikaRT::nn::QMoEWoQ": errors on a
+codes before touching the device.  The device pointers here are fake: no
+call below may reach a launch (moe_prepare is only called on unbound
+layers, which it rejects first) (clika "ClikaRT::nn::QMoEWoQ": errors on a
 geometry mismatch, a bias without its declared slot, a still-unbound slot).
 """
 import ctypes as C
@@ -72,6 +74,16 @@ def test_create_rejects_bad_geometry(L, kw):
     assert not h.value
 
 
+def bound_status(L, h, H, E, x_dtype):
+    """Binding check without any device work: a forward on T = 0 tokens
+    validates the slots and returns before anything is launched."""
+    x = _t(L, [0, H], x_dtype)
+    lg = _t(L, [0, E], L.MOE_DTYPE_F32)
+    o = _t(L, [0, H], x_dtype)
+    return L.lib().moe_forward(h, C.byref(x), C.byref(lg), None, C.byref(o), None, 0,
+                               None, None)
+
+
 def _t(L, shape, dtype, ptr=0x1000, scales=None):
     m = L.moe_tensor()
     m.data = ptr
@@ -90,15 +102,17 @@ def test_set_weights_validation(L):
     lib = L.lib()
     BF = L.MOE_DTYPE_BF16
     w = L.moe_weights()
-    # forward/prepare before binding: UNBOUND
+    # forward/prepare before binding: UNBOUND (checked before any device work)
     assert lib.moe_prepare(h, None) == 4
+    assert bound_status(L, h, 64, 8, BF) == 4
     w.gate_up_experts = _t(L, [8, 64, 64], BF)
     w.down_experts = _t(L, [8, 64, 32], BF)
     assert lib.moe_set_weights(h, C.byref(w)) == 0
     assert lib.moe_prepare(h, None) == 4        # declared gate_up_bias unbound
+    assert bound_status(L, h, 64, 8, BF) == 4
     w.gate_up_bias = _t(L, [8, 64], BF)
     assert lib.moe_set_weights(h, C.byref(w)) == 0
-    assert lib.moe_prepare(h, None) == 0
+    assert bound_status(L, h, 64, 8, BF) == 0
     w.down_bias = _t(L, [8, 64], BF)            # not declared
     assert lib.moe_set_weights(h, C.byref(w)) == 3
     w.down_bias = L.moe_tensor()
@@ -127,7 +141,7 @@ def test_unfused_and_mxfp4_binding(L):
     assert lib.moe_set_weights(h, C.byref(w)) == 2
     w.gate_experts = _t(L, [8, 32, 64], MX, scales=0x4000)
     assert lib.moe_set_weights(h, C.byref(w)) == 0
-    assert lib.moe_prepare(h, None) == 0
+    assert bound_status(L, h, 64, 8, L.MOE_DTYPE_BF16) == 0
     lib.moe_destroy(h)
 
 

@@ -73,7 +73,7 @@ def test_activations(act):
     compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"activation {act}")
 
 
-@pytest.mark.parametrize("routing", [
+ROUTING_MODES = [
     dict(scoring="softmax", renormalize=False),
     dict(scoring="softmax", renormalize=True, routed_scaling_factor=2.5),
     dict(scoring="sigmoid", renormalize=False),
@@ -82,13 +82,46 @@ def test_activations(act):
     dict(scoring="sigmoid", renormalize=True, selection_bias_std=0.1, n_group=8,
          topk_group=3, routed_scaling_factor=1.5),
     dict(scoring="softmax", renormalize=True, n_group=4, topk_group=2),
-])
-def test_routing_modes(routing):
+]
+
+
+@pytest.mark.parametrize("routing", ROUTING_MODES)
+def test_routing_modes_f32(routing):
+    """Every routing mode (MoeSpec `score`, `selection_bias`, `groups`,
+    `renormalize`, `scale`) on an f32 layer, 1e-4 bar: without
+    renormalisation the outputs are heavy-tailed (max |out| ~ 15 RMS), where
+    rounding the oracle itself to bf16 already exceeds 2e-2 of the RMS."""
+    cfg = synth.MoeConfig(name="rt", cid=203, T=700, H=128, I=64, E=64, K=6,
+                          x_dtype="f32", w_dtype="f32", **routing)
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, _ = run_gpu(cfg, inp)
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], "f32", f"routing f32 {routing}")
+
+
+@pytest.mark.parametrize("routing", [m for m in ROUTING_MODES if m["renormalize"]])
+def test_routing_modes_bf16(routing):
     cfg = synth.MoeConfig(name="rt", cid=203, T=700, H=128, I=64, E=64, K=6, **routing)
     inp = synth.make_inputs(cfg, device=DEV)
     out, r, _ = run_gpu(cfg, inp)
     check_routing(cfg, inp, r, cfg.T)
-    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"routing {routing}")
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"routing bf16 {routing}")
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+def test_h_overflow_falls_back_to_bf16(variant):
+    """h beyond fp16's range in some tiles: those tiles are stored in bf16 and
+    the down GEMM of their rows runs in bf16 (fp16 tiles rounded to bf16)."""
+    cfg = synth.MoeConfig(name="ovf", cid=208, T=40, H=64, I=256, E=4, K=2)
+    inp = synth.make_inputs(cfg, device=DEV)
+    w = inp["gate_up_experts"].float()
+    w[:, :128] *= 300.0                      # gate rows of h columns 0..127
+    w[:, cfg.I:cfg.I + 128] *= 300.0         # their up rows
+    inp["gate_up_experts"] = w.to(torch.bfloat16)
+    ref = oracle_full(cfg, inp)
+    assert np.abs(ref["out"]).max() > 0
+    out, r, _ = run_gpu(cfg, inp, gemm_variant=variant)
+    compare_out(out, ref["out"], "bf16", f"h overflow variant {variant}")
 
 
 # ------------------------------------------------------------------ edge cases
