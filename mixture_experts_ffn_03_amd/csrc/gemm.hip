@@ -33,6 +33,8 @@
 // quantised).
 #include "gemm_common.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -132,6 +134,109 @@ __device__ inline f32x16 mfma(const u32x4 &a, const u32x4 &b, const f32x16 &c)
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Epilogue shared by both GEMM kernels: lane holds output features
+// 8*i4 + 4*(lane/32) + j (j = 0..3) of token lane % 32 of each 32x32 block.
+template <class TL, bool GATED>
+__device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
+                                         f32x16 (&acc)[TL::FN][TL::FM], float *s_red)
+{
+    constexpr int NWAVES = TL::NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave % TL::WN, wm = wave / TL::WN;
+    const int lrow = lane & 31;
+    const int fq = (lane >> 5) * 4;
+    if (GATED) {
+        // pass 1: activation into the gate accumulators, tile max |h|
+        const int64_t eb = (int64_t)tw.e * g.w.e_rows;
+        float hmax = 0.0f;
+#pragma unroll
+        for (int fp = 0; fp < TL::FN / 2; ++fp)
+#pragma unroll
+            for (int m = 0; m < TL::FM; ++m) {
+                const bool tok_ok = wm * TL::TM + m * 32 + lrow < tw.nrows;
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int c = tw.n0 + wn * (TL::TN / 2) + fp * 32 + i4 * 8 + fq;
+                    const bool ok = tok_ok && c < g.Nout;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float gv = acc[fp][m][i4 * 4 + j];
+                        float uv = acc[fp + TL::FN / 2][m][i4 * 4 + j];
+                        if (ok && g.w.b_gate)
+                            gv += bias_at(g.w.b_gate,
+                                          eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_gate);
+                        if (ok && g.w.b_up)
+                            uv += bias_at(g.w.b_up,
+                                          eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_up);
+                        const float h = gated_act(g.act, gv, uv, g.alpha, g.beta, g.limit);
+                        acc[fp][m][i4 * 4 + j] = h;
+                        if (ok) hmax = fmaxf(hmax, fabsf(h));
+                    }
+                }
+            }
+        // block max -> storage format of this h tile
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, off, 64));
+        if (lane == 0) s_red[wave] = hmax;
+        __syncthreads();
+        float bmax = s_red[0];
+#pragma unroll
+        for (int w = 1; w < NWAVES; ++w) bmax = fmaxf(bmax, s_red[w]);
+        const bool f16 = g.f16_ok && bmax <= 65504.0f;
+        if (tid == 0) g.hfmt[(int64_t)tw.mg * g.h_tiles + tw.nt] = f16 ? kHF16 : kHBF16;
+        // pass 2: store h
+        uint16_t *h = (uint16_t *)g.out;
+#pragma unroll
+        for (int fp = 0; fp < TL::FN / 2; ++fp)
+#pragma unroll
+            for (int m = 0; m < TL::FM; ++m) {
+                const int tl = wm * TL::TM + m * 32 + lrow;
+                if (tl >= tw.nrows) continue;
+                uint16_t *hrow = h + (int64_t)(tw.row0 + tl) * g.Nout;
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int c = tw.n0 + wn * (TL::TN / 2) + fp * 32 + i4 * 8 + fq;
+                    if (c >= g.Nout) continue;
+                    const f32x16 &a = acc[fp][m];
+                    const int r0 = i4 * 4;
+                    if (f16) {
+                        f16x4 o = {(_Float16)a[r0], (_Float16)a[r0 + 1], (_Float16)a[r0 + 2],
+                                   (_Float16)a[r0 + 3]};
+                        *(f16x4 *)(hrow + c) = o;
+                    } else {
+                        bf16x4 o = {(__bf16)a[r0], (__bf16)a[r0 + 1], (__bf16)a[r0 + 2],
+                                    (__bf16)a[r0 + 3]};
+                        *(bf16x4 *)(hrow + c) = o;
+                    }
+                }
+            }
+    } else {
+        float *y = (float *)g.out;
+        const int64_t eb = (int64_t)tw.e * g.w.e_rows;
+#pragma unroll
+        for (int f = 0; f < TL::FN; ++f)
+#pragma unroll
+            for (int m = 0; m < TL::FM; ++m) {
+                const int tl = wm * TL::TM + m * 32 + lrow;
+                if (tl >= tw.nrows) continue;
+                float *yrow = y + (int64_t)(tw.row0 + tl) * g.Nout;
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int c = tw.n0 + wn * TL::TN + f * 32 + i4 * 8 + fq;
+                    if (c >= g.Nout) continue;
+                    f32x4 o;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float v = acc[f][m][i4 * 4 + j];
+                        if (g.w.b_gate) v += bias_at(g.w.b_gate, eb + c + j);
+                        o[j] = v;
+                    }
+                    *(f32x4 *)(yrow + c) = o;
+                }
+            }
+    }
 }
 
 // One tile.  F16: operands of the MFMA are fp16 (down GEMM whose h tiles are
@@ -291,98 +396,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g, const TileWork &tw,
         __syncthreads();
     }
 
-    // ---- epilogue: lane holds features 8*i4 + 4*(lane/32) + j of token lane%32
-    const int fq = (lane >> 5) * 4;
-    if (GATED) {
-        // pass 1: activation into the gate accumulators, tile max |h|
-        const int64_t eb = (int64_t)tw.e * g.w.e_rows;
-        float hmax = 0.0f;
-#pragma unroll
-        for (int fp = 0; fp < TL::FN / 2; ++fp)
-#pragma unroll
-            for (int m = 0; m < TL::FM; ++m) {
-                const bool tok_ok = wm * TL::TM + m * 32 + lrow < tw.nrows;
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const int c = tw.n0 + wn * (TL::TN / 2) + fp * 32 + i4 * 8 + fq;
-                    const bool ok = tok_ok && c < g.Nout;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float gv = acc[fp][m][i4 * 4 + j];
-                        float uv = acc[fp + TL::FN / 2][m][i4 * 4 + j];
-                        if (ok && g.w.b_gate)
-                            gv += bias_at(g.w.b_gate,
-                                          eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_gate);
-                        if (ok && g.w.b_up)
-                            uv += bias_at(g.w.b_up,
-                                          eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_up);
-                        const float h = gated_act(g.act, gv, uv, g.alpha, g.beta, g.limit);
-                        acc[fp][m][i4 * 4 + j] = h;
-                        if (ok) hmax = fmaxf(hmax, fabsf(h));
-                    }
-                }
-            }
-        // block max -> storage format of this h tile
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, off, 64));
-        if (lane == 0) s_red[wave] = hmax;
-        __syncthreads();
-        float bmax = s_red[0];
-#pragma unroll
-        for (int w = 1; w < NWAVES; ++w) bmax = fmaxf(bmax, s_red[w]);
-        const bool f16 = g.f16_ok && bmax <= 65504.0f;
-        if (tid == 0) g.hfmt[(int64_t)tw.mg * g.h_tiles + tw.nt] = f16 ? kHF16 : kHBF16;
-        // pass 2: store h
-        uint16_t *h = (uint16_t *)g.out;
-#pragma unroll
-        for (int fp = 0; fp < TL::FN / 2; ++fp)
-#pragma unroll
-            for (int m = 0; m < TL::FM; ++m) {
-                const int tl = wm * TL::TM + m * 32 + lrow;
-                if (tl >= tw.nrows) continue;
-                uint16_t *hrow = h + (int64_t)(tw.row0 + tl) * g.Nout;
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const int c = tw.n0 + wn * (TL::TN / 2) + fp * 32 + i4 * 8 + fq;
-                    if (c >= g.Nout) continue;
-                    const f32x16 &a = acc[fp][m];
-                    const int r0 = i4 * 4;
-                    if (f16) {
-                        f16x4 o = {(_Float16)a[r0], (_Float16)a[r0 + 1], (_Float16)a[r0 + 2],
-                                   (_Float16)a[r0 + 3]};
-                        *(f16x4 *)(hrow + c) = o;
-                    } else {
-                        bf16x4 o = {(__bf16)a[r0], (__bf16)a[r0 + 1], (__bf16)a[r0 + 2],
-                                    (__bf16)a[r0 + 3]};
-                        *(bf16x4 *)(hrow + c) = o;
-                    }
-                }
-            }
-    } else {
-        float *y = (float *)g.out;
-        const int64_t eb = (int64_t)tw.e * g.w.e_rows;
-#pragma unroll
-        for (int f = 0; f < TL::FN; ++f)
-#pragma unroll
-            for (int m = 0; m < TL::FM; ++m) {
-                const int tl = wm * TL::TM + m * 32 + lrow;
-                if (tl >= tw.nrows) continue;
-                float *yrow = y + (int64_t)(tw.row0 + tl) * g.Nout;
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const int c = tw.n0 + wn * TL::TN + f * 32 + i4 * 8 + fq;
-                    if (c >= g.Nout) continue;
-                    f32x4 o;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float v = acc[f][m][i4 * 4 + j];
-                        if (g.w.b_gate) v += bias_at(g.w.b_gate, eb + c + j);
-                        o[j] = v;
-                    }
-                    *(f32x4 *)(yrow + c) = o;
-                }
-            }
-    }
+    epilogue<TL, GATED>(g, tw, acc, s_red);
 }
 
 template <class TL, bool MX, bool GATED>
@@ -412,6 +426,259 @@ hipError_t launch(const GemmArgs &a, int64_t max_m_tiles, hipStream_t s)
 {
     const int64_t grid = max_m_tiles * a.nN + 8;
     gemm_kernel<TL, MX, GATED><<<dim3((unsigned)grid), dim3(TL::NT), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel for 16-bit weights: gfx950 direct global->LDS loads.
+//
+// Each k-step's A and B panels are fetched by global_load_lds_dwordx4 (16 bytes
+// per lane straight into LDS, no staging registers) into one of S LDS stages;
+// S-1 k-steps are in flight while one is computed.  One barrier per k-step,
+// preceded by a wait for this thread's own loads of the step about to be read.
+// LDS rows are BK*2 bytes; the 16-byte chunk c of row r sits at physical chunk
+// c ^ sw(r).  gfx950 serves a 16-byte-per-lane LDS read 16 lanes at a time
+// across 64 four-byte banks (measured: this swizzle has no bank conflicts,
+// one built for 8 lanes / 32 banks had a conflict on half the LDS cycles), so
+// the 16 lanes that read one chunk column of 16 consecutive rows must land in
+// 16 different 16-byte bank groups.  Each load instruction of a wave fills
+// one contiguous KiB of LDS; the swizzle is applied by choosing which global
+// chunk each lane fetches.
+//
+// Operand conversion happens after the LDS read, in registers: fp16 down GEMM
+// steps convert the bf16 weight fragments to fp16 (exact, range checked at
+// prepare); bf16 down GEMM steps round fp16-stored h fragments to bf16.
+// A ragged last k-step loads clamped in-row addresses and zeroes the operand
+// fragments past the reduction length.
+
+template <int BN_, int BM_, int BK_, int WN_, int WM_, int S_>
+struct DTile {
+    static constexpr int BN = BN_, BM = BM_, BK = BK_, WN = WN_, WM = WM_, S = S_;
+    static constexpr int NT = 64 * WN * WM;
+    static constexpr int NWAVES = WN * WM;
+    static constexpr int TN = BN / WN, TM = BM / WM;
+    static constexpr int FN = TN / 32, FM = TM / 32;
+    static constexpr int CPR = BK / 8;                  // 16-byte chunks per row
+    static constexpr int ROWB = BK * 2;                 // bytes per LDS row
+    static constexpr int NA = BM * CPR / NT;            // A loads per thread per step
+    static constexpr int NB = BN * CPR / NT;            // B loads per thread per step
+    static constexpr int L = NA + NB;
+    static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static_assert(NA * NT == BM * CPR && NB * NT == BN * CPR, "whole loads per thread");
+    static_assert(NA >= 1 && NB >= 1, "every thread loads A and B");
+    static_assert(FN >= 2 && FN % 2 == 0, "gate/up pairs per wave");
+    static_assert(S >= 2 && (S - 2) * L <= 63, "vmcnt range");
+    static_assert(S * STAGE + (kMaxExperts + 1) * 4 + 64 <= 160 * 1024, "LDS");
+    // swizzle of row r: rows r and r + 16/CPR start in the same bank group
+    __device__ static inline int sw(int r) { return (r / (16 / CPR)) % CPR; }
+    static_assert(CPR == 4 || CPR == 8 || CPR == 16, "row of 64, 128 or 256 bytes");
+};
+
+using PrefillDTile = DTile<256, 256, 32, 4, 2, 4>;   // 512 threads, 4 x 32 KiB stages
+using DecodeDTile = DTile<256, 32, 64, 4, 1, 4>;     // 256 threads, 4 x 36 KiB stages
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes
+// LDS bytes [m0 + 16 l, m0 + 16 l + 16).  Issued as inline asm so that the
+// compiler inserts no waits of its own for it: every wait on these loads is
+// the explicit vmcnt in wait_loads_barrier.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_byte)
+{
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_byte) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
+// Wait until at most N of this thread's DMA loads are outstanding and all of
+// its LDS reads have returned, then synchronise the workgroup.
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <class TL, bool GATED, bool F16>
+__device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, uint8_t *lds,
+                                         float *s_red)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int Kd = g.Kd;
+
+    // ---- per-load global sources: row base + swizzled chunk
+    const uint8_t *a_src[TL::NA];
+    int a_k[TL::NA];                   // first k of the chunk this load fetches
+#pragma unroll
+    for (int i = 0; i < TL::NA; ++i) {
+        const int q = (i * TL::NWAVES + wave) * 64 + lane;   // LDS chunk index
+        const int row = q / TL::CPR, p = q % TL::CPR;
+        const int c = p ^ TL::sw(row);
+        const int r = tw.row0 + min(row, tw.nrows - 1);
+        const int src = g.row_token ? g.row_token[r] : r;
+        a_k[i] = c * 8;
+        a_src[i] = (const uint8_t *)g.a + ((int64_t)src * Kd + c * 8) * 2;
+    }
+    const uint8_t *b_src[TL::NB];
+    int b_k[TL::NB];
+#pragma unroll
+    for (int i = 0; i < TL::NB; ++i) {
+        const int q = (i * TL::NWAVES + wave) * 64 + lane;
+        const int row = q / TL::CPR, p = q % TL::CPR;
+        const int c = p ^ TL::sw(row);
+        const bool up = GATED && row >= TL::BN / 2;
+        const int f = min(tw.n0 + (up ? row - TL::BN / 2 : row), g.Nout - 1);
+        const int64_t wrow = (int64_t)tw.e * g.w.e_rows + (int64_t)f * g.w.row_mul +
+                             (up ? g.w.off_up : g.w.off_gate);
+        const void *base = up ? g.w.w_up : g.w.w_gate;
+        b_k[i] = c * 8;
+        b_src[i] = (const uint8_t *)base + (wrow * Kd + c * 8) * 2;
+    }
+
+    // LDS byte offset of this wave's first KiB of a stage (wave-uniform)
+    const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds_offset(lds) + wave * 1024);
+    const int nk = (Kd + TL::BK - 1) / TL::BK;
+    const int nfull = Kd / TL::BK;       // k-steps with no chunk past Kd
+    auto issue = [&](int kt) {
+        const uint32_t st = wave_lds + (kt % TL::S) * TL::STAGE;
+        const int k0 = kt * TL::BK;
+        const bool full = kt < nfull;
+#pragma unroll
+        for (int i = 0; i < TL::NA; ++i) {
+            // a chunk past the reduction length re-reads the row start (ignored)
+            const uint8_t *src = (full || k0 + a_k[i] < Kd) ? a_src[i] + 2 * k0
+                                                             : a_src[i] - 2 * a_k[i];
+            dma16(src, st + i * TL::NWAVES * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < TL::NB; ++i) {
+            const uint8_t *src = (full || k0 + b_k[i] < Kd) ? b_src[i] + 2 * k0
+                                                             : b_src[i] - 2 * b_k[i];
+            dma16(src, st + TL::A_BYTES + i * TL::NWAVES * 1024);
+        }
+    };
+
+    // ---- fragment addressing (row r of a 32-row block = lane % 32)
+    const int wn = wave % TL::WN, wm = wave / TL::WN;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    const int lsw = TL::sw(lrow);
+    auto brow = [&](int f) {
+        if (GATED)
+            return (f < TL::FN / 2) ? wn * (TL::TN / 2) + f * 32
+                                    : TL::BN / 2 + wn * (TL::TN / 2) + (f - TL::FN / 2) * 32;
+        return wn * TL::TN + f * 32;
+    };
+    // byte offset in a row of logical chunk c for this lane
+    auto chunk_off = [&](int c) { return ((c ^ lsw) & (TL::CPR - 1)) * 16; };
+
+    const uint8_t *hf = GATED ? nullptr : g.hfmt + (int64_t)tw.mg * g.h_tiles;
+
+    f32x16 acc[TL::FN][TL::FM];
+#pragma unroll
+    for (int f = 0; f < TL::FN; ++f)
+#pragma unroll
+        for (int m = 0; m < TL::FM; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[f][m][r] = 0.0f;
+
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    // MV: 32-row token blocks of this wave that hold rows (the others skip
+    // their LDS reads and MFMAs; an expert's last tile is usually short)
+    auto compute = [&](int kt, auto tail_tag, auto mv_tag) {
+        constexpr bool tail = decltype(tail_tag)::value;
+        constexpr int MV = decltype(mv_tag)::value;
+        const uint8_t *st = lds + (kt % TL::S) * TL::STAGE;
+        const int k0 = kt * TL::BK;
+        // bf16 down GEMM: fp16-stored h of this step is rounded to bf16
+        const bool a_f16 = !GATED && !F16 && hf[k0 / g.h_width] == kHF16;
+#pragma unroll
+        for (int ks = 0; ks < TL::BK / 16; ++ks) {
+            const int c = ks * 2 + lhalf;
+            const int coff = chunk_off(c);
+            const bool kval = !tail || k0 + c * 8 < Kd;   // chunk inside the reduction
+            u32x4 bf[TL::FN], af[TL::FM];
+#pragma unroll
+            for (int f = 0; f < TL::FN; ++f) {
+                bf[f] = *(const u32x4 *)(st + TL::A_BYTES + (brow(f) + lrow) * TL::ROWB + coff);
+                if (tail && !kval) bf[f] = zero4;
+                if (F16) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) bf[f][w] = bf16x2_to_f16x2(bf[f][w]);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MV; ++m) {
+                af[m] = *(const u32x4 *)(st + (wm * TL::TM + m * 32 + lrow) * TL::ROWB + coff);
+                if (tail && !kval) af[m] = zero4;
+                if (a_f16) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) af[m][w] = f16x2_to_bf16x2(af[m][w]);
+                }
+            }
+#pragma unroll
+            for (int f = 0; f < TL::FN; ++f)
+#pragma unroll
+                for (int m = 0; m < MV; ++m)
+                    acc[f][m] = mfma<F16>(bf[f], af[m], acc[f][m]);
+        }
+    };
+
+    auto kloop = [&](auto mv_tag) {
+#pragma unroll
+        for (int s = 0; s < TL::S - 1; ++s)
+            if (s < nk) issue(s);
+        for (int kt = 0; kt < nfull; ++kt) {
+            // this thread's loads of step kt are done once at most (S-2) steps
+            // of later loads are pending; then every wave's are (barrier)
+            if (kt + TL::S - 2 < nk) wait_loads_barrier<(TL::S - 2) * TL::L>();
+            else wait_loads_barrier<0>();
+            if (kt + TL::S - 1 < nk) issue(kt + TL::S - 1);
+            compute(kt, std::false_type{}, mv_tag);
+        }
+        if (nfull < nk) {   // ragged last step (its loads were issued in the loop)
+            wait_loads_barrier<0>();
+            compute(nfull, std::true_type{}, mv_tag);
+        }
+    };
+    // every wave runs the same loads and barriers; only its MFMA work differs
+    const int mv = min(max((tw.nrows - wm * TL::TM + 31) / 32, 0), TL::FM);
+    if (mv == TL::FM) kloop(std::integral_constant<int, TL::FM>{});
+    else if (TL::FM > 1 && mv == 1) kloop(std::integral_constant<int, 1>{});
+    else if (TL::FM > 2 && mv == 2) kloop(std::integral_constant<int, (TL::FM > 2 ? 2 : 1)>{});
+    else if (TL::FM > 3 && mv == 3) kloop(std::integral_constant<int, (TL::FM > 3 ? 3 : 1)>{});
+    else kloop(std::integral_constant<int, 0>{});
+    // all waves are done reading LDS before the epilogue reuses s_red / exits
+    __syncthreads();
+    epilogue<TL, GATED>(g, tw, acc, s_red);
+}
+
+template <class TL, bool GATED>
+__global__ __launch_bounds__(TL::NT) void gemm_dma_kernel(GemmArgs g)
+{
+    constexpr int NW = GATED ? TL::BN / 2 : TL::BN;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[TL::S * TL::STAGE];
+    __shared__ int s_cum[kMaxExperts + 1];
+    __shared__ float s_red[TL::NWAVES];
+
+    TileWork tw;
+    if (!find_tile(g, s_cum, TL::BM, NW, &tw)) return;
+    if (GATED) {
+        dma_body<TL, GATED, false>(g, tw, lds, s_red);
+        return;
+    }
+    const uint8_t *hf = g.hfmt + (int64_t)tw.mg * g.h_tiles;
+    int all16 = g.f16_ok;
+    for (int i = threadIdx.x; i < g.h_tiles; i += TL::NT) all16 &= hf[i] == kHF16;
+    if (__syncthreads_and(all16)) dma_body<TL, GATED, true>(g, tw, lds, s_red);
+    else dma_body<TL, GATED, false>(g, tw, lds, s_red);
+}
+
+template <class TL, bool GATED>
+hipError_t launch_dma(const GemmArgs &a, int64_t max_m_tiles, hipStream_t s)
+{
+    const int64_t grid = max_m_tiles * a.nN + 8;
+    gemm_dma_kernel<TL, GATED><<<dim3((unsigned)grid), dim3(TL::NT), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -446,6 +713,14 @@ __global__ __launch_bounds__(256) void weight_range_kernel(const uint32_t *w, co
 
 }  // namespace
 
+// The MXFP4 (register-staged) and 16-bit (DMA) kernels of one variant share
+// their tile shape, which the host uses for scheduling and the h formats.
+static_assert(PrefillTile::BM == PrefillDTile::BM && PrefillTile::BN == PrefillDTile::BN, "");
+static_assert(DecodeTile::BM == DecodeDTile::BM && DecodeTile::BN == DecodeDTile::BN, "");
+static_assert((PrefillTile::BN / 2) % PrefillDTile::BK == 0 && (DecodeTile::BN / 2) % DecodeDTile::BK == 0 &&
+              (PrefillTile::BN / 2) % PrefillTile::BK == 0 && (DecodeTile::BN / 2) % DecodeTile::BK == 0,
+              "a down-GEMM k-step lies inside one h tile");
+
 int gemm_bm(GemmKind kind)
 {
     return kind == GemmKind::kPrefill ? PrefillTile::BM : DecodeTile::BM;
@@ -464,14 +739,14 @@ hipError_t launch_gemm_bf16(GemmKind kind, bool gated, bool mxfp4, const GemmArg
         if (mxfp4)
             return gated ? launch<PrefillTile, true, true>(a, max_m_tiles, s)
                          : launch<PrefillTile, true, false>(a, max_m_tiles, s);
-        return gated ? launch<PrefillTile, false, true>(a, max_m_tiles, s)
-                     : launch<PrefillTile, false, false>(a, max_m_tiles, s);
+        return gated ? launch_dma<PrefillDTile, true>(a, max_m_tiles, s)
+                     : launch_dma<PrefillDTile, false>(a, max_m_tiles, s);
     }
     if (mxfp4)
         return gated ? launch<DecodeTile, true, true>(a, max_m_tiles, s)
                      : launch<DecodeTile, true, false>(a, max_m_tiles, s);
-    return gated ? launch<DecodeTile, false, true>(a, max_m_tiles, s)
-                 : launch<DecodeTile, false, false>(a, max_m_tiles, s);
+    return gated ? launch_dma<DecodeDTile, true>(a, max_m_tiles, s)
+                 : launch_dma<DecodeDTile, false>(a, max_m_tiles, s);
 }
 
 hipError_t launch_weight_range(const void *w, const uint8_t *scales, int64_t n_words,
