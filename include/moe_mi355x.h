@@ -155,9 +155,9 @@ moe_status moe_options_default(moe_options *opts);
 /* Declare a layer (QMoEWoQ::make / clika MoE.__init__): geometry E, H, I,
  * top_k (1 <= top_k <= min(E, 64)), the expert weight dtype (F32, BF16 or
  * MXFP4), which bias slots exist, and the options (NULL = defaults).
- * Validation: E <= 1024; with a group limit, E % n_group == 0 and
- * top_k <= topk_group * E / n_group; MXFP4 needs H and I multiples of 32;
- * dense weights need H and I multiples of 8.  The handle owns no device
+ * Validation: E <= 1024; H <= 2^20; I <= 131072; with a group limit,
+ * E % n_group == 0 and top_k <= topk_group * E / n_group; MXFP4 needs H and I
+ * multiples of 32; dense weights need H and I multiples of 8.  The handle owns no device
  * memory.  Errors: INVALID_ARGUMENT. */
 moe_status moe_create(int64_t num_experts, int64_t hidden_size,
                       int64_t intermediate_size, int64_t top_k,

@@ -365,8 +365,9 @@ moe_status moe_create(int64_t E, int64_t H, int64_t I, int64_t K, moe_dtype wdty
     if (K < 1 || K > E || K > kMaxTopK)
         return fail(MOE_ERR_INVALID_ARGUMENT, "top_k %lld outside 1..min(E, %d)", (long long)K,
                     kMaxTopK);
-    if (H < 1 || I < 1 || H > (1 << 20) || I > (1 << 20))
-        return fail(MOE_ERR_INVALID_ARGUMENT, "hidden/intermediate size out of range");
+    if (H < 1 || I < 1 || H > (1 << 20) || I > kMaxHTiles * 128)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "hidden size above 2^20 or intermediate size "
+                    "above %d", kMaxHTiles * 128);
     if (wdtype != MOE_DTYPE_F32 && wdtype != MOE_DTYPE_BF16 && wdtype != MOE_DTYPE_MXFP4)
         return fail(MOE_ERR_INVALID_ARGUMENT, "weight dtype must be F32, BF16 or MXFP4");
     if (wdtype == MOE_DTYPE_MXFP4 && (H % 32 || I % 32))

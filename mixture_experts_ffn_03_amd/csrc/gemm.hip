@@ -451,9 +451,10 @@ hipError_t launch(const GemmArgs &a, int64_t max_m_tiles, hipStream_t s)
 // A ragged last k-step loads clamped in-row addresses and zeroes the operand
 // fragments past the reduction length.
 
-template <int BN_, int BM_, int BK_, int WN_, int WM_, int S_>
+template <int BN_, int BM_, int BK_, int WN_, int WM_, int SA_, int SB_>
 struct DTile {
-    static constexpr int BN = BN_, BM = BM_, BK = BK_, WN = WN_, WM = WM_, S = S_;
+    static constexpr int BN = BN_, BM = BM_, BK = BK_, WN = WN_, WM = WM_;
+    static constexpr int SA = SA_, SB = SB_;            // LDS stages of A and of B
     static constexpr int NT = 64 * WN * WM;
     static constexpr int NWAVES = WN * WM;
     static constexpr int TN = BN / WN, TM = BM / WM;
@@ -462,21 +463,28 @@ struct DTile {
     static constexpr int ROWB = BK * 2;                 // bytes per LDS row
     static constexpr int NA = BM * CPR / NT;            // A loads per thread per step
     static constexpr int NB = BN * CPR / NT;            // B loads per thread per step
-    static constexpr int L = NA + NB;
     static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int B_BASE = SA * A_BYTES;         // B stages follow the A stages
+    static constexpr int LDS_BYTES = SA * A_BYTES + SB * B_BYTES;
     static_assert(NA * NT == BM * CPR && NB * NT == BN * CPR, "whole loads per thread");
     static_assert(NA >= 1 && NB >= 1, "every thread loads A and B");
     static_assert(FN >= 2 && FN % 2 == 0, "gate/up pairs per wave");
-    static_assert(S >= 2 && (S - 2) * L <= 63, "vmcnt range");
-    static_assert(S * STAGE + (kMaxExperts + 1) * 4 + 64 <= 160 * 1024, "LDS");
+    static_assert(SA == 2 && SB >= SA && SB <= 4, "A one step ahead, B up to three");
+    static_assert(2 * NB <= 63, "vmcnt range");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(LDS_BYTES >= (kMaxExperts + 1) * 4 && LDS_BYTES >= NWAVES * 4,
+                  "scheduling table and epilogue scratch overlay the stages");
     // swizzle of row r: rows r and r + 16/CPR start in the same bank group
     __device__ static inline int sw(int r) { return (r / (16 / CPR)) % CPR; }
     static_assert(CPR == 4 || CPR == 8 || CPR == 16, "row of 64, 128 or 256 bytes");
 };
 
-using PrefillDTile = DTile<256, 256, 32, 4, 2, 4>;   // 512 threads, 4 x 32 KiB stages
-using DecodeDTile = DTile<256, 32, 64, 4, 1, 4>;     // 256 threads, 4 x 36 KiB stages
+// 512 threads, wave 64x128; k-steps of 64 (128-byte rows: a 64-byte row
+// piece halves the L2->LDS rate); A (token rows, L2/MALL resident) two
+// stages, B (weights, first touch from HBM) three: 2 x 32 + 3 x 32 KiB.
+using PrefillDTile = DTile<256, 256, 64, 4, 2, 2, 3>;
+// 256 threads, wave 64x32; weights stream from HBM: four B stages.
+using DecodeDTile = DTile<256, 32, 64, 4, 1, 2, 4>;
 
 // 16 bytes per lane from global memory straight into LDS: lane l writes
 // LDS bytes [m0 + 16 l, m0 + 16 l + 16).  Issued as inline asm so that the
@@ -499,6 +507,10 @@ __device__ __forceinline__ void wait_loads_barrier()
 {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+
+// 16 zero bytes in global memory: the source of every DMA chunk past the
+// reduction length, so a ragged last k-step needs no masking.
+__device__ const u32x4 g_zero16 = {0u, 0u, 0u, 0u};
 
 template <class TL, bool GATED, bool F16>
 __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, uint8_t *lds,
@@ -535,28 +547,29 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
         b_k[i] = c * 8;
         b_src[i] = (const uint8_t *)base + (wrow * Kd + c * 8) * 2;
     }
+    const uint8_t *zero = (const uint8_t *)&g_zero16;
 
     // LDS byte offset of this wave's first KiB of a stage (wave-uniform)
     const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds_offset(lds) + wave * 1024);
     const int nk = (Kd + TL::BK - 1) / TL::BK;
     const int nfull = Kd / TL::BK;       // k-steps with no chunk past Kd
-    auto issue = [&](int kt) {
-        const uint32_t st = wave_lds + (kt % TL::S) * TL::STAGE;
+    auto issue_a = [&](int kt) {
+        const uint32_t st = wave_lds + (kt % TL::SA) * TL::A_BYTES;
         const int k0 = kt * TL::BK;
         const bool full = kt < nfull;
 #pragma unroll
-        for (int i = 0; i < TL::NA; ++i) {
-            // a chunk past the reduction length re-reads the row start (ignored)
-            const uint8_t *src = (full || k0 + a_k[i] < Kd) ? a_src[i] + 2 * k0
-                                                             : a_src[i] - 2 * a_k[i];
-            dma16(src, st + i * TL::NWAVES * 1024);
-        }
+        for (int i = 0; i < TL::NA; ++i)
+            dma16((full || k0 + a_k[i] < Kd) ? a_src[i] + 2 * k0 : zero,
+                  st + i * TL::NWAVES * 1024);
+    };
+    auto issue_b = [&](int kt) {
+        const uint32_t st = wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
+        const int k0 = kt * TL::BK;
+        const bool full = kt < nfull;
 #pragma unroll
-        for (int i = 0; i < TL::NB; ++i) {
-            const uint8_t *src = (full || k0 + b_k[i] < Kd) ? b_src[i] + 2 * k0
-                                                             : b_src[i] - 2 * b_k[i];
-            dma16(src, st + TL::A_BYTES + i * TL::NWAVES * 1024);
-        }
+        for (int i = 0; i < TL::NB; ++i)
+            dma16((full || k0 + b_k[i] < Kd) ? b_src[i] + 2 * k0 : zero,
+                  st + i * TL::NWAVES * 1024);
     };
 
     // ---- fragment addressing (row r of a 32-row block = lane % 32)
@@ -569,9 +582,9 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
                                     : TL::BN / 2 + wn * (TL::TN / 2) + (f - TL::FN / 2) * 32;
         return wn * TL::TN + f * 32;
     };
-    // byte offset in a row of logical chunk c for this lane
-    auto chunk_off = [&](int c) { return ((c ^ lsw) & (TL::CPR - 1)) * 16; };
 
+    // h formats of these rows (bf16 down GEMM only; read from global memory,
+    // whose waits only ever lengthen the explicit ones)
     const uint8_t *hf = GATED ? nullptr : g.hfmt + (int64_t)tw.mg * g.h_tiles;
 
     f32x16 acc[TL::FN][TL::FM];
@@ -582,63 +595,115 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[f][m][r] = 0.0f;
 
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    constexpr int NKS = TL::BK / 16;     // MFMA sub-steps per k-step
+    static_assert(NKS % 2 == 0, "fragment ping-pong over an even number of sub-steps");
+
     // MV: 32-row token blocks of this wave that hold rows (the others skip
     // their LDS reads and MFMAs; an expert's last tile is usually short)
-    auto compute = [&](int kt, auto tail_tag, auto mv_tag) {
-        constexpr bool tail = decltype(tail_tag)::value;
+    auto kloop = [&](auto mv_tag) {
         constexpr int MV = decltype(mv_tag)::value;
-        const uint8_t *st = lds + (kt % TL::S) * TL::STAGE;
-        const int k0 = kt * TL::BK;
-        // bf16 down GEMM: fp16-stored h of this step is rounded to bf16
-        const bool a_f16 = !GATED && !F16 && hf[k0 / g.h_width] == kHF16;
-#pragma unroll
-        for (int ks = 0; ks < TL::BK / 16; ++ks) {
-            const int c = ks * 2 + lhalf;
-            const int coff = chunk_off(c);
-            const bool kval = !tail || k0 + c * 8 < Kd;   // chunk inside the reduction
-            u32x4 bf[TL::FN], af[TL::FM];
+        u32x4 bf[2][TL::FN], af[2][TL::FM > 0 ? TL::FM : 1];
+        // read the fragments of sub-step ks of k-step kt into buffer b
+        auto read = [&](int kt, int ks, int b) {
+            const uint8_t *sa = lds + (kt % TL::SA) * TL::A_BYTES;
+            const uint8_t *sb = lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
+            const int coff = ((ks * 2 + lhalf) ^ lsw) * 16;
+            // bf16 down GEMM: an fp16-stored h step is rounded to bf16
+            const bool a_f16 = !GATED && !F16 && hf[(kt * TL::BK) / g.h_width] == kHF16;
 #pragma unroll
             for (int f = 0; f < TL::FN; ++f) {
-                bf[f] = *(const u32x4 *)(st + TL::A_BYTES + (brow(f) + lrow) * TL::ROWB + coff);
-                if (tail && !kval) bf[f] = zero4;
+                bf[b][f] = *(const u32x4 *)(sb + (brow(f) + lrow) * TL::ROWB + coff);
                 if (F16) {
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) bf[f][w] = bf16x2_to_f16x2(bf[f][w]);
+                    for (int w = 0; w < 4; ++w) bf[b][f][w] = bf16x2_to_f16x2(bf[b][f][w]);
                 }
             }
 #pragma unroll
             for (int m = 0; m < MV; ++m) {
-                af[m] = *(const u32x4 *)(st + (wm * TL::TM + m * 32 + lrow) * TL::ROWB + coff);
-                if (tail && !kval) af[m] = zero4;
+                af[b][m] = *(const u32x4 *)(sa + (wm * TL::TM + m * 32 + lrow) * TL::ROWB + coff);
                 if (a_f16) {
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) af[m][w] = f16x2_to_bf16x2(af[m][w]);
+                    for (int w = 0; w < 4; ++w) af[b][m][w] = f16x2_to_bf16x2(af[b][m][w]);
                 }
             }
+        };
+        auto mma = [&](int b) {
 #pragma unroll
             for (int f = 0; f < TL::FN; ++f)
 #pragma unroll
                 for (int m = 0; m < MV; ++m)
-                    acc[f][m] = mfma<F16>(bf[f], af[m], acc[f][m]);
-        }
-    };
-
-    auto kloop = [&](auto mv_tag) {
+                    acc[f][m] = mfma<F16>(bf[b][f], af[b][m], acc[f][m]);
+        };
+        // Barrier of step j: A(j) and B(j) are in LDS and every wave has
+        // finished reading step j-1, whose stages A(j+1) and B(j+SB-1) then
+        // refill.  Issue order: prologue B(0), A(0), B(1), ..., B(SB-2);
+        // after barrier j the group A(j+1), B(j+SB-1).  Loads complete in
+        // issue order, so A(j) and B(j) (issued before A(j)) are done once at
+        // most the loads issued after A(j) are pending: B(j+SB-2) for j >= 1,
+        // B(1..SB-2) for j = 0.
+        auto issue_group = [&](int j) {
+            if (j + 1 < nk) issue_a(j + 1);
+            if (j + TL::SB - 1 < nk) issue_b(j + TL::SB - 1);
+        };
+        // the same group, load by load, spread over the sub-steps of step j
+        // (a burst of DMA issues stalls the wave before its MFMAs); the
+        // order of issue, which the waits rely on, is unchanged
+        auto issue_group_part = [&](int j, int part) {
+            constexpr int L = TL::NA + TL::NB;
+            const uint32_t sta = wave_lds + ((j + 1) % TL::SA) * TL::A_BYTES;
+            const uint32_t stb = wave_lds + TL::B_BASE + ((j + TL::SB - 1) % TL::SB) * TL::B_BYTES;
+            const int ka = (j + 1) * TL::BK, kb = (j + TL::SB - 1) * TL::BK;
+            const bool fa = j + 1 < nfull, fb = j + TL::SB - 1 < nfull;
 #pragma unroll
-        for (int s = 0; s < TL::S - 1; ++s)
-            if (s < nk) issue(s);
-        for (int kt = 0; kt < nfull; ++kt) {
-            // this thread's loads of step kt are done once at most (S-2) steps
-            // of later loads are pending; then every wave's are (barrier)
-            if (kt + TL::S - 2 < nk) wait_loads_barrier<(TL::S - 2) * TL::L>();
+            for (int q = 0; q < L; ++q) {
+                if (q < part * L / NKS || q >= (part + 1) * L / NKS) continue;
+                if (q < TL::NA) {
+                    const int i = q;
+                    if (j + 1 < nk)
+                        dma16((fa || ka + a_k[i] < Kd) ? a_src[i] + 2 * ka : zero,
+                              sta + i * TL::NWAVES * 1024);
+                } else {
+                    const int i = q - TL::NA;
+                    if (j + TL::SB - 1 < nk)
+                        dma16((fb || kb + b_k[i] < Kd) ? b_src[i] + 2 * kb : zero,
+                              stb + i * TL::NWAVES * 1024);
+                }
+            }
+        };
+        issue_b(0);
+        issue_a(0);
+#pragma unroll
+        for (int s = 1; s < TL::SB - 1; ++s)
+            if (s < nk) issue_b(s);
+        {
+            const int after = min(TL::SB - 2, nk - 1);     // B steps issued after A(0)
+            if (after >= 2) wait_loads_barrier<2 * TL::NB>();
+            else if (after == 1) wait_loads_barrier<TL::NB>();
             else wait_loads_barrier<0>();
-            if (kt + TL::S - 1 < nk) issue(kt + TL::S - 1);
-            compute(kt, std::false_type{}, mv_tag);
+            static_assert(TL::SB - 2 <= 2, "prologue wait cases");
         }
-        if (nfull < nk) {   // ragged last step (its loads were issued in the loop)
-            wait_loads_barrier<0>();
-            compute(nfull, std::true_type{}, mv_tag);
+        issue_group(0);
+        auto step_barrier = [&](int j) {
+            // (with SB = 2, B(j) follows A(j) in its group: wait for all)
+            if (TL::SB >= 3 && j + TL::SB - 2 < nk) wait_loads_barrier<TL::NB>();
+            else wait_loads_barrier<0>();
+        };
+        read(0, 0, 0);
+        for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int cur = ks & 1;
+                if (kt > 0) issue_group_part(kt, ks);   // group 0 went out whole
+                if (ks + 1 < NKS) {
+                    read(kt, ks + 1, cur ^ 1);
+                } else if (kt + 1 < nk) {
+                    // the MFMAs of the previous sub-step keep the matrix
+                    // pipe busy through the barrier
+                    step_barrier(kt + 1);
+                    read(kt + 1, 0, cur ^ 1);
+                }
+                mma(cur);
+            }
         }
     };
     // every wave runs the same loads and barriers; only its MFMA work differs
@@ -648,7 +713,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     else if (TL::FM > 2 && mv == 2) kloop(std::integral_constant<int, (TL::FM > 2 ? 2 : 1)>{});
     else if (TL::FM > 3 && mv == 3) kloop(std::integral_constant<int, (TL::FM > 3 ? 3 : 1)>{});
     else kloop(std::integral_constant<int, 0>{});
-    // all waves are done reading LDS before the epilogue reuses s_red / exits
+    // all waves are done reading LDS before the epilogue reuses it as scratch
     __syncthreads();
     epilogue<TL, GATED>(g, tw, acc, s_red);
 }
@@ -657,21 +722,39 @@ template <class TL, bool GATED>
 __global__ __launch_bounds__(TL::NT) void gemm_dma_kernel(GemmArgs g)
 {
     constexpr int NW = GATED ? TL::BN / 2 : TL::BN;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[TL::S * TL::STAGE];
-    __shared__ int s_cum[kMaxExperts + 1];
-    __shared__ float s_red[TL::NWAVES];
+    // one LDS allocation: the scheduling table, then the stages, then the
+    // epilogue scratch use it in turn
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[TL::LDS_BYTES];
+    int *s_cum = (int *)lds;
+    float *s_red = (float *)lds;
 
     TileWork tw;
     if (!find_tile(g, s_cum, TL::BM, NW, &tw)) return;
-    if (GATED) {
-        dma_body<TL, GATED, false>(g, tw, lds, s_red);
-        return;
+    bool f16 = false;
+    if (!GATED) {
+        // down GEMM: fp16 operands iff every h tile of these rows is fp16
+        const uint8_t *hf = g.hfmt + (int64_t)tw.mg * g.h_tiles;
+        int all16 = g.f16_ok;
+        for (int i = threadIdx.x; i < g.h_tiles; i += TL::NT) all16 &= hf[i] == kHF16;
+        // block AND through an LDS word (the library's own reduction would
+        // need LDS beyond the stages)
+        volatile int *flag = (volatile int *)lds;
+        __syncthreads();                     // every s_cum read is done
+        if (threadIdx.x == 0) *flag = 1;
+        __syncthreads();
+        if (!all16) *flag = 0;
+        __syncthreads();
+        f16 = *flag != 0;
+        __syncthreads();                     // before the loads overwrite it
+    } else {
+        __syncthreads();                     // every s_cum read is done
     }
-    const uint8_t *hf = g.hfmt + (int64_t)tw.mg * g.h_tiles;
-    int all16 = g.f16_ok;
-    for (int i = threadIdx.x; i < g.h_tiles; i += TL::NT) all16 &= hf[i] == kHF16;
-    if (__syncthreads_and(all16)) dma_body<TL, GATED, true>(g, tw, lds, s_red);
-    else dma_body<TL, GATED, false>(g, tw, lds, s_red);
+    if constexpr (GATED) {
+        dma_body<TL, true, false>(g, tw, lds, s_red);
+    } else {
+        if (f16) dma_body<TL, false, true>(g, tw, lds, s_red);
+        else dma_body<TL, false, false>(g, tw, lds, s_red);
+    }
 }
 
 template <class TL, bool GATED>

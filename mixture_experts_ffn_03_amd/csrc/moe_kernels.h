@@ -12,6 +12,7 @@ constexpr int kMaxExperts = 1024;   // routing keeps E/64 experts per lane
 constexpr int kMaxTopK = 64;        // one lane per kept slot
 constexpr int kMaxGroups = 64;      // one lane per group score
 constexpr int kPermTokens = 256;    // tokens per permutation block
+constexpr int kMaxHTiles = 1024;    // h tiles per row (I <= 1024 * 128)
 
 struct RouteArgs {
     const float *logits;     // [T, E]
