@@ -512,7 +512,9 @@ __device__ __forceinline__ void wait_loads_barrier()
 // reduction length, so a ragged last k-step needs no masking.
 __device__ const u32x4 g_zero16 = {0u, 0u, 0u, 0u};
 
-template <class TL, bool GATED, bool F16>
+// RAGGED: the reduction length is not a multiple of BK (the last k-step's
+// chunks past it read zeros); otherwise no k-step needs a bounds test.
+template <class TL, bool GATED, bool F16, bool RAGGED>
 __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, uint8_t *lds,
                                          float *s_red)
 {
@@ -552,14 +554,14 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     // LDS byte offset of this wave's first KiB of a stage (wave-uniform)
     const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds_offset(lds) + wave * 1024);
     const int nk = (Kd + TL::BK - 1) / TL::BK;
-    const int nfull = Kd / TL::BK;       // k-steps with no chunk past Kd
+    const int nfull = RAGGED ? Kd / TL::BK : nk;    // k-steps with no chunk past Kd
     auto issue_a = [&](int kt) {
         const uint32_t st = wave_lds + (kt % TL::SA) * TL::A_BYTES;
         const int k0 = kt * TL::BK;
         const bool full = kt < nfull;
 #pragma unroll
         for (int i = 0; i < TL::NA; ++i)
-            dma16((full || k0 + a_k[i] < Kd) ? a_src[i] + 2 * k0 : zero,
+            dma16((!RAGGED || full || k0 + a_k[i] < Kd) ? a_src[i] + 2 * k0 : zero,
                   st + i * TL::NWAVES * 1024);
     };
     auto issue_b = [&](int kt) {
@@ -568,7 +570,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
         const bool full = kt < nfull;
 #pragma unroll
         for (int i = 0; i < TL::NB; ++i)
-            dma16((full || k0 + b_k[i] < Kd) ? b_src[i] + 2 * k0 : zero,
+            dma16((!RAGGED || full || k0 + b_k[i] < Kd) ? b_src[i] + 2 * k0 : zero,
                   st + i * TL::NWAVES * 1024);
     };
 
@@ -660,12 +662,12 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
                 if (q < TL::NA) {
                     const int i = q;
                     if (j + 1 < nk)
-                        dma16((fa || ka + a_k[i] < Kd) ? a_src[i] + 2 * ka : zero,
+                        dma16((!RAGGED || fa || ka + a_k[i] < Kd) ? a_src[i] + 2 * ka : zero,
                               sta + i * TL::NWAVES * 1024);
                 } else {
                     const int i = q - TL::NA;
                     if (j + TL::SB - 1 < nk)
-                        dma16((fb || kb + b_k[i] < Kd) ? b_src[i] + 2 * kb : zero,
+                        dma16((!RAGGED || fb || kb + b_k[i] < Kd) ? b_src[i] + 2 * kb : zero,
                               stb + i * TL::NWAVES * 1024);
                 }
             }
@@ -749,11 +751,18 @@ __global__ __launch_bounds__(TL::NT) void gemm_dma_kernel(GemmArgs g)
     } else {
         __syncthreads();                     // every s_cum read is done
     }
+    const bool ragged = g.Kd % TL::BK != 0;
     if constexpr (GATED) {
-        dma_body<TL, true, false>(g, tw, lds, s_red);
+        if (ragged) dma_body<TL, true, false, true>(g, tw, lds, s_red);
+        else dma_body<TL, true, false, false>(g, tw, lds, s_red);
     } else {
-        if (f16) dma_body<TL, false, true>(g, tw, lds, s_red);
-        else dma_body<TL, false, false>(g, tw, lds, s_red);
+        if (f16) {
+            if (ragged) dma_body<TL, false, true, true>(g, tw, lds, s_red);
+            else dma_body<TL, false, true, false>(g, tw, lds, s_red);
+        } else {
+            if (ragged) dma_body<TL, false, false, true>(g, tw, lds, s_red);
+            else dma_body<TL, false, false, false>(g, tw, lds, s_red);
+        }
     }
 }
 
