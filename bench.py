@@ -85,8 +85,10 @@ def load_traffic(workload: str):
         return None
 
 
-def cpu_baseline(cfg, inp, budget_s: float):
-    """The oracle on the host cores over a bounded token sample."""
+def cpu_baseline(cfg, inp, budget_s: float, stream_bytes=None):
+    """The oracle on the host cores over a bounded token sample.  With
+    stream_bytes (a decode step) and the whole step in the sample, the rate is
+    those weight bytes over the oracle's time, as for the GPU line."""
     import numpy as np
     import oracle
     oracle.build()
@@ -103,11 +105,13 @@ def cpu_baseline(cfg, inp, budget_s: float):
     t0 = time.perf_counter()
     oracle.forward(p, host, tokens=toks, threads=threads)
     dt = time.perf_counter() - t0
-    flops = 6.0 * cfg.K * cfg.H * cfg.I * len(toks)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+    if stream_bytes is not None and len(toks) == cfg.T:
+        value, unit = stream_bytes / dt / 1e9, "GB/s"
+    else:
+        value, unit = 6.0 * cfg.K * cfg.H * cfg.I * len(toks) / dt / 1e12, "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"{len(toks)} of {cfg.T} tokens of {cfg.name} (full weights), "
-                      f"{dt:.1f} s on {threads} threads; {len(toks) / dt:.2f} tokens/s"}
+                      f"{dt:.3g} s on {threads} threads; {len(toks) / dt:.2f} tokens/s"}
 
 
 def main():
@@ -139,6 +143,14 @@ def main():
     x, lg = inp["x"], inp["logits"]
     out = torch.empty_like(x)
     ws = layer.workspace(cfg.T, dev)
+    # experts that receive tokens (their weights are the ones a step streams)
+    touched = int((layer.route(lg)["expert_counts"] > 0).sum().item())
+    wb = 0.5 + 1.0 / 32.0 if cfg.w_dtype == "mxfp4" else (4.0 if cfg.w_dtype == "f32" else 2.0)
+    gu_bytes = 2.0 * cfg.I * cfg.H * wb
+    dn_bytes = 1.0 * cfg.H * cfg.I * wb
+    # few rows per expert: the step streams weights (same threshold the library
+    # uses to pick its small-M tiles)
+    decode = cfg.T * cfg.K < 96 * cfg.E
     torch.cuda.synchronize()
 
     if args.copy_calibration:
@@ -175,12 +187,26 @@ def main():
     flops = float(cfg.flops)
     gemm1_flops = 4.0 * cfg.T * cfg.K * cfg.H * cfg.I
     g1 = stage_ms["gemm_gate_up"]
-    achieved = gemm1_flops / (g1 * 1e-3) / 1e12
     traffic = load_traffic(cfg.name)
+    if decode:
+        # weight-stream rate: each touched expert's weights are read once per step
+        stream = touched * (gu_bytes + dn_bytes)
+        value, unit = stream / (ms * 1e-3) / 1e9, "GB/s"
+        g1_bytes = touched * gu_bytes + cfg.T * cfg.H * 2 + cfg.T * cfg.K * cfg.I * 2
+        roof = {"bound": "hbm", "kernel": "gate||up grouped GEMM (decode tiles)",
+                "achieved": g1_bytes / (g1 * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+        roof = {"bound": "mfma", "kernel": "gate||up grouped GEMM",
+                "achieved": gemm1_flops / (g1 * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
     res = {
         "metric": METRIC,
-        "value": flops / (ms * 1e-3) / 1e12,
-        "unit": "TFLOP/s",
+        "value": value,
+        "unit": unit,
         "tokens_per_s": cfg.T / (ms * 1e-3),
         "n_gpus": 1,
         "steps": args.steps,
@@ -195,14 +221,16 @@ def main():
                    "K": cfg.K, "layout": cfg.layout, "weights": cfg.w_dtype,
                    "scoring": cfg.scoring, "parallelism": "none (1 GPU)"},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "roofline": {"bound": "mfma", "kernel": "gate||up grouped GEMM",
-                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic},
+        "active_tflops": flops / (ms * 1e-3) / 1e12,
+        "weight_stream_gbs": touched * (gu_bytes + dn_bytes) / (ms * 1e-3) / 1e9,
+        "experts_touched": touched,
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(
+            cfg, inp, args.cpu_seconds,
+            stream_bytes=touched * (gu_bytes + dn_bytes) if decode else None)
     print(json.dumps(res), flush=True)
 
 

@@ -7,6 +7,7 @@ are cited by title and section/field.
 """
 import itertools
 import math
+import os
 
 import numpy as np
 import pytest
@@ -394,9 +395,19 @@ def test_clamped_swiglu_reduces_to_silu_and_clamps(orc):
 
 # --------------------------------------------------------------- MXFP4 pins
 
-# OCP Microscaling Formats (MX) v1.0, FP4 E2M1 element encodings (code -> value)
-E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
-        -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+def _load_e2m1():
+    """FP4 E2M1 code -> value, from the OCP MX v1.0 table in tests/golden."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "e2m1_table.txt")
+    table = {}
+    for line in open(path):
+        line = line.split("#", 1)[0].split()
+        if line:
+            table[int(line[0])] = float(line[1])
+    assert sorted(table) == list(range(16))
+    return [table[c] for c in range(16)]
+
+
+E2M1 = _load_e2m1()
 
 
 def test_mxfp4_decode_exhaustive(orc):
