@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gemm-variant", type=int, default=0,
+                    help="grouped-GEMM tiles: 0 auto, 1 256-row, 2 32-row, 3 128-row")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain device copy of known size (HBM counter calibration)")
     args = ap.parse_args()
@@ -138,7 +140,7 @@ def main():
     dev = torch.device("cuda:0")
     log(f"[bench] generating {cfg.name} inputs on {dev}")
     inp = synth.make_inputs(cfg, device=dev)
-    layer = from_config(cfg)
+    layer = from_config(cfg, gemm_variant=args.gemm_variant)
     layer.set_weights_from(inp)
     x, lg = inp["x"], inp["logits"]
     out = torch.empty_like(x)

@@ -95,9 +95,11 @@ typedef struct moe_options {
     float swiglu_alpha;           /* default 1                                       */
     float swiglu_beta;            /* default 0                                       */
     float swiglu_limit;           /* default 0 = no clamp                            */
-    int32_t gemm_variant;         /* grouped-GEMM tiles: 0 auto (by rows per expert),
-                                     1 large-M (prefill) tiles, 2 small-M (decode)
-                                     tiles; f32 layers ignore it.  Default 0       */
+    int32_t gemm_variant;         /* grouped-GEMM tiles: 0 auto (by rows per expert
+                                     and weight type), 1 large-M (prefill, 256-row)
+                                     tiles, 2 small-M (decode, 32-row) tiles, 3
+                                     mid (128-row) tiles; f32 layers ignore it.
+                                     Default 0                                     */
 } moe_options;
 
 /* A device tensor view.  ndim == 0 (or data == NULL) marks an absent tensor.

@@ -25,10 +25,15 @@ struct moe_layer {
     moe_weights w;
     bool bound;
     // Prepared state (QMoEWoQ "pack once, thread-safe"): whether the down
-    // weights convert exactly to fp16, which enables the fp16 down GEMM.
+    // weights convert exactly to fp16, which enables the fp16 down GEMM, and
+    // for MXFP4 weights the library-owned packed copy the GEMMs stream
+    // (allocated at the first prepare, sized by the geometry alone, refilled
+    // by every later prepare, freed by moe_destroy).
     mutable std::mutex mu;
     mutable bool prepared;
     mutable int down_f16_ok;
+    mutable uint8_t *mx_pack = nullptr;
+    mutable int64_t mx_off[4] = {0, 0, 0, 0};   // codes 1, scales 1, codes 2, scales 2
 };
 
 namespace {
@@ -154,7 +159,7 @@ Workspace layout(const moe_layer *l, int64_t T)
     // one h-format byte per (GEMM-1 M-tile, GEMM-1 feature tile), worst case
     // over the two 16-bit kernel variants
     size_t nfmt = 0;
-    for (GemmKind k : {GemmKind::kPrefill, GemmKind::kDecode}) {
+    for (GemmKind k : {GemmKind::kPrefill, GemmKind::kDecode, GemmKind::kMid}) {
         const int64_t ntile = (l->I + gemm_bn(k, true) - 1) / gemm_bn(k, true);
         const size_t n = (size_t)(max_m_tiles_of(l, T, gemm_bm(k)) * ntile);
         if (n > nfmt) nfmt = n;
@@ -166,29 +171,42 @@ Workspace layout(const moe_layer *l, int64_t T)
     return w;
 }
 
-// Kernel variant: f32 layers use the f32 kernels; otherwise the small-M
-// (decode) tiles when the average expert holds few rows.
-enum class Path { kF32, kPrefill, kDecode };
+// Kernel variant: f32 layers use the f32 kernels; otherwise by the average
+// rows per expert: small-M (decode, 32-row) tiles below 96, mid (128-row)
+// tiles for MXFP4 weights below 512, else the large-M (256-row) tiles.
+enum class Path { kF32, kPrefill, kDecode, kMid };
 
 Path choose_path(const moe_layer *l, int64_t T)
 {
     if (l->wdtype == MOE_DTYPE_F32) return Path::kF32;
     if (l->opts.gemm_variant == 1) return Path::kPrefill;
     if (l->opts.gemm_variant == 2) return Path::kDecode;
+    if (l->opts.gemm_variant == 3) return Path::kMid;
     const double rows_per_expert = (double)(T * l->K) / (double)l->E;
-    return rows_per_expert < 96.0 ? Path::kDecode : Path::kPrefill;
+    if (rows_per_expert < 96.0) return Path::kDecode;
+    // MXFP4 weight stages are small, so 128-row tiles cost little in loads
+    // and avoid a mostly empty second tile per expert
+    if (l->wdtype == MOE_DTYPE_MXFP4 && rows_per_expert < 512.0) return Path::kMid;
+    return Path::kPrefill;
+}
+
+GemmKind kind_of(Path p)
+{
+    return p == Path::kPrefill ? GemmKind::kPrefill
+           : p == Path::kMid   ? GemmKind::kMid
+                               : GemmKind::kDecode;
 }
 
 int path_bm(Path p)
 {
     if (p == Path::kF32) return gemm_f32_bm();
-    return gemm_bm(p == Path::kPrefill ? GemmKind::kPrefill : GemmKind::kDecode);
+    return gemm_bm(kind_of(p));
 }
 
 int path_bn(Path p, bool gated)
 {
     if (p == Path::kF32) return gemm_f32_bn(gated);
-    return gemm_bn(p == Path::kPrefill ? GemmKind::kPrefill : GemmKind::kDecode, gated);
+    return gemm_bn(kind_of(p), gated);
 }
 
 moe_status hip_check(hipError_t e, const char *what)
@@ -300,11 +318,75 @@ moe_status check_workspace(const moe_layer *l, int64_t T, void *ws, size_t bytes
 // Prepare once per binding: scan the down-weight range on `s` and decide
 // whether the down GEMM may run in fp16 (bf16 magnitudes <= 65280, or MXFP4
 // scale bytes in [104, 140], convert exactly).  Synchronises `s` once.
+// Pack an MXFP4 layer's gate||up (GEMM 1, two operands) and down (GEMM 2)
+// stacks into l->mx_pack.
+moe_status pack_mxfp4(const moe_layer *l, hipStream_t s)
+{
+    const int64_t E = l->E, H = l->H, I = l->I;
+    const int64_t sz[4] = {mx_pack_bytes(2, I, H, E), mx_pack_scale_bytes(2, I, H, E),
+                           mx_pack_bytes(1, H, I, E), mx_pack_scale_bytes(1, H, I, E)};
+    if (!l->mx_pack) {
+        int64_t total = 0;
+        for (int i = 0; i < 4; ++i) {
+            l->mx_off[i] = total;
+            total += (sz[i] + 255) / 256 * 256;
+        }
+        void *p = nullptr;
+        moe_status st = hip_check(hipMalloc(&p, (size_t)total), "MXFP4 pack alloc");
+        if (st) return st;
+        l->mx_pack = (uint8_t *)p;
+    }
+    PackArgs a{};
+    a.E = (int)E;
+    a.ops = 2;
+    a.Nh = (int)I;
+    a.K = (int)H;
+    a.nks = (int)((H + 63) / 64);
+    if (fused(l)) {
+        a.codes[0] = a.codes[1] = (const uint8_t *)l->w.gate_up_experts.data;
+        a.scales[0] = a.scales[1] = l->w.gate_up_experts.scales;
+        a.e_rows = 2 * I;
+        const bool il = l->opts.swiglu_fusion == MOE_FUSION_INTERLEAVED;
+        a.row_mul = il ? 2 : 1;
+        a.off[0] = 0;
+        a.off[1] = il ? 1 : (int)I;
+    } else {
+        a.codes[0] = (const uint8_t *)l->w.gate_experts.data;
+        a.scales[0] = l->w.gate_experts.scales;
+        a.codes[1] = (const uint8_t *)l->w.gate_up_experts.data;
+        a.scales[1] = l->w.gate_up_experts.scales;
+        a.e_rows = I;
+        a.row_mul = 1;
+        a.off[0] = a.off[1] = 0;
+    }
+    a.pk = l->mx_pack + l->mx_off[0];
+    a.pks = l->mx_pack + l->mx_off[1];
+    moe_status st = hip_check(launch_mx_pack(a, s), "MXFP4 pack (gate/up)");
+    if (st) return st;
+    PackArgs d{};
+    d.E = (int)E;
+    d.ops = 1;
+    d.Nh = (int)H;
+    d.K = (int)I;
+    d.nks = (int)((I + 63) / 64);
+    d.codes[0] = d.codes[1] = (const uint8_t *)l->w.down_experts.data;
+    d.scales[0] = d.scales[1] = l->w.down_experts.scales;
+    d.e_rows = H;
+    d.row_mul = 1;
+    d.pk = l->mx_pack + l->mx_off[2];
+    d.pks = l->mx_pack + l->mx_off[3];
+    return hip_check(launch_mx_pack(d, s), "MXFP4 pack (down)");
+}
+
 moe_status prepare_locked(const moe_layer *l, hipStream_t s)
 {
     std::lock_guard<std::mutex> lock(l->mu);
     if (l->prepared) return MOE_OK;
     int ok = 0;
+    if (l->wdtype == MOE_DTYPE_MXFP4) {
+        moe_status st = pack_mxfp4(l, s);
+        if (st) return st;
+    }
     if (l->wdtype != MOE_DTYPE_F32) {
         uint32_t *d = nullptr;
         moe_status st = hip_check(hipMalloc((void **)&d, 16), "prepare alloc");
@@ -392,7 +474,7 @@ moe_status moe_create(int64_t E, int64_t H, int64_t I, int64_t K, moe_dtype wdty
         return fail(MOE_ERR_INVALID_ARGUMENT, "unknown activation %d", o.activation);
     if (o.swiglu_fusion < MOE_FUSION_NONE || o.swiglu_fusion > MOE_FUSION_SPLIT)
         return fail(MOE_ERR_INVALID_ARGUMENT, "unknown swiglu_fusion %d", o.swiglu_fusion);
-    if (o.gemm_variant < 0 || o.gemm_variant > 2)
+    if (o.gemm_variant < 0 || o.gemm_variant > 3)
         return fail(MOE_ERR_INVALID_ARGUMENT, "unknown gemm_variant %d", o.gemm_variant);
     if (!(o.routed_scaling_factor == o.routed_scaling_factor))
         return fail(MOE_ERR_INVALID_ARGUMENT, "routed_scaling_factor is NaN");
@@ -632,6 +714,16 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     g2.h_tiles = g1.nN;
     g2.h_width = bn1;
     g2.f16_ok = g1.f16_ok;
+    if (mx) {
+        g1.pk = l->mx_pack + l->mx_off[0];
+        g1.pks = l->mx_pack + l->mx_off[1];
+        g1.nks = (int)((l->H + 63) / 64);
+        g1.nrb_half = (int)(l->I / 32);
+        g2.pk = l->mx_pack + l->mx_off[2];
+        g2.pks = l->mx_pack + l->mx_off[3];
+        g2.nks = (int)((l->I + 63) / 64);
+        g2.nrb_half = (int)(l->H / 32);
+    }
 
     if (max_m_tiles * (g1.nN > g2.nN ? g1.nN : g2.nN) + 8 > 0x7fffffffLL)
         return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch");
@@ -641,7 +733,7 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
         if ((st = mark(3))) return st;
         if ((st = hip_check(launch_gemm_f32(false, g2, max_m_tiles, s), "gemm2 launch"))) return st;
     } else {
-        const GemmKind kind = path == Path::kPrefill ? GemmKind::kPrefill : GemmKind::kDecode;
+        const GemmKind kind = kind_of(path);
         if ((st = hip_check(launch_gemm_bf16(kind, true, mx, g1, max_m_tiles, s), "gemm1 launch")))
             return st;
         if ((st = mark(3))) return st;
@@ -668,6 +760,7 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
 
 moe_status moe_destroy(moe_layer *l)
 {
+    if (l && l->mx_pack) (void)hipFree(l->mx_pack);
     delete l;
     return MOE_OK;
 }

@@ -2,10 +2,10 @@
 //
 // Each workgroup computes one tile of Y^T = W_e * A^T for one expert e:
 // BN weight rows (output features) by BM permutation rows (tokens), fp32
-// accumulation, reduction in BK-wide steps through double-buffered LDS.
-// The weight panel is the MFMA "A" operand and the token panel the "B"
-// operand, so each lane ends with four consecutive output features of one
-// token -- 8-byte 16-bit / 16-byte f32 stores in the epilogue.
+// accumulation, reduction in 64-wide k-steps through LDS stages filled by
+// direct global->LDS loads.  The weight panel is the MFMA "A" operand and the
+// token panel the "B" operand, so each lane ends with four consecutive output
+// features of one token -- 8-byte 16-bit / 16-byte f32 stores in the epilogue.
 //
 // Two epilogues:
 //  gated  (gate||up GEMM, ONNX "MoE" fc1/fc3): the BN weight rows of a tile
@@ -17,20 +17,21 @@
 //         exactly, else in bf16; one format byte per tile records the choice.
 //  down   (ONNX "MoE" fc2): when every h tile of its rows is fp16 (the
 //         normal case), a workgroup converts the bf16 (or MXFP4) down weights
-//         exactly to fp16 on their way into LDS and runs the f16 MFMA;
-//         otherwise it rounds the fp16 h tiles to bf16 and runs the bf16 MFMA.
-//         Adds the down bias and stores y in f32; the combine rounds once,
-//         after the weighted sum.
+//         exactly to fp16 after their LDS read and runs the f16 MFMA;
+//         otherwise it rounds the fp16 h fragments to bf16 and runs the bf16
+//         MFMA.  Adds the down bias and stores y in f32; the combine rounds
+//         once, after the weighted sum.
 //
-// The A operand of the gated GEMM is gathered straight from x through the
+// The token operand of the gated GEMM is gathered straight from x through the
 // permutation (row_token), so the permuted activations are never written.
 //
-// MXFP4 weights ("ClikaRT::nn::QMoEWoQ": decode one block at a time inside
-// the GEMM dot, never a dense copy): each 16-byte code chunk is one 32-element
-// block; it is decoded with its e8m0 scale by the gfx950 scaled conversion
-// (exact: e2m1 times a power of two fits the 16-bit format) on its way into
-// LDS, and the MFMA stays 16-bit x 16-bit (weight-only; the activation is not
-// quantised).
+// MXFP4 weights ("ClikaRT::nn::QMoEWoQ": weight-only, decoded one block at a
+// time inside the GEMM, never a dense copy): the packed codes and e8m0 scales
+// travel to LDS at 4.25 bits per weight; after the LDS read each lane turns
+// its 8 codes of a sub-step into 8 16-bit values with the gfx950 scaled
+// conversion (exact: e2m1 times a power of two fits bf16, and fp16 for the
+// scale range the prepare-time check admits), and the MFMA stays 16-bit x
+// 16-bit (the activation is not quantised).
 #include "gemm_common.h"
 
 #include <type_traits>
@@ -48,29 +49,6 @@ typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-template <int BN_, int BM_, int BK_, int WN_, int WM_>
-struct Tile {
-    static constexpr int BN = BN_, BM = BM_, BK = BK_, WN = WN_, WM = WM_;
-    static constexpr int NT = 64 * WN * WM;          // threads
-    static constexpr int TN = BN / WN, TM = BM / WM; // wave tile
-    static constexpr int FN = TN / 32, FM = TM / 32; // 32x32 MFMA blocks per wave
-    static constexpr int LDK = BK + 8;               // padded LDS row (elements)
-    static constexpr int CPR = BK / 8;               // 16-byte 16-bit chunks per row
-    static constexpr int QPR = BK / 32;              // 16-byte MXFP4 chunks per row
-    static constexpr int A_CH = BM * CPR / NT;
-    static constexpr int B_CH_BF16 = BN * CPR / NT;
-    static constexpr int B_CH_MX = BN * QPR / NT;
-    static constexpr int STAGE = (BM + BN) * LDK;    // elements per LDS stage
-    static_assert(A_CH * NT == BM * CPR, "A tile chunks");
-    static_assert(B_CH_BF16 * NT == BN * CPR, "B tile chunks");
-    static_assert(B_CH_MX * NT == BN * QPR, "MXFP4 tile chunks");
-    static_assert(FN >= 2 && FN % 2 == 0, "gate/up pairs per wave");
-    static_assert(2 * STAGE * 2 + (kMaxExperts + 1) * 4 + 64 <= 160 * 1024, "LDS");
-};
-
-using PrefillTile = Tile<256, 256, 64, 4, 2>;   // 512 threads, wave 64x128
-using DecodeTile = Tile<256, 32, 128, 4, 1>;    // 256 threads, wave 64x32
 
 __device__ inline float bias_at(const void *b, int64_t i)
 {
@@ -102,28 +80,24 @@ __device__ inline uint32_t f16x2_to_bf16x2(uint32_t w)
     return __builtin_bit_cast(uint32_t, b);
 }
 
-// 32 MXFP4 elements (16 code bytes, element 2i in the low nibble of byte i)
-// times 2^(X-127) -> 32 16-bit values (bf16 or fp16) in `dst` (16-byte aligned).
+// Eight MXFP4 elements (one code word, element 2i in the low nibble of byte
+// i) times the e8m0 multiplier sc -> eight 16-bit values (bf16 or fp16).
 template <bool F16>
-__device__ inline void decode_mxfp4(const u32x4 &codes, float sc, uint16_t *dst)
+__device__ inline u32x4 decode_mxfp4_8(uint32_t word, float sc)
 {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t word = codes[w];
-        u32x4 o;
-        if (F16) {
-            o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc, 0));
-            o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc, 1));
-            o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc, 2));
-            o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc, 3));
-        } else {
-            o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0));
-            o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1));
-            o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2));
-            o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3));
-        }
-        *(u32x4 *)(dst + w * 8) = o;
+    u32x4 o;
+    if (F16) {
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc, 0));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc, 1));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc, 2));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc, 3));
+    } else {
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3));
     }
+    return o;
 }
 
 template <bool F16>
@@ -239,242 +213,73 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
     }
 }
 
-// One tile.  F16: operands of the MFMA are fp16 (down GEMM whose h tiles are
-// all fp16); otherwise bf16.
-template <class TL, bool MX, bool GATED, bool F16>
-__device__ __forceinline__ void gemm_body(const GemmArgs &g, const TileWork &tw,
-                                          uint16_t *lds, float *s_red)
-{
-    constexpr int B_CH = MX ? TL::B_CH_MX : TL::B_CH_BF16;
-    constexpr int NWAVES = TL::NT / 64;
-    const int tid = threadIdx.x;
-    const int Kd = g.Kd;
-
-    // ---- A (token) rows: gathered through the permutation when row_token is set
-    const int a_kc = (tid % TL::CPR) * 8;
-    const uint16_t *a_ptr[TL::A_CH];
-    int a_lr[TL::A_CH];
-#pragma unroll
-    for (int i = 0; i < TL::A_CH; ++i) {
-        const int lr = tid / TL::CPR + i * (TL::NT / TL::CPR);
-        const int r = tw.row0 + min(lr, tw.nrows - 1);
-        const int src = g.row_token ? g.row_token[r] : r;
-        a_lr[i] = lr;
-        a_ptr[i] = (const uint16_t *)g.a + (int64_t)src * Kd + a_kc;
-    }
-
-    // ---- B (weight) rows
-    constexpr int BPR = MX ? TL::QPR : TL::CPR;       // chunks per row
-    const int b_kc = tid % BPR;
-    const uint8_t *b_ptr[B_CH];
-    const uint8_t *s_ptr[B_CH];
-    int b_lr[B_CH];
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-        const int lr = tid / BPR + i * (TL::NT / BPR);
-        const bool up = GATED && lr >= TL::BN / 2;
-        const int c = min(tw.n0 + (up ? lr - TL::BN / 2 : lr), g.Nout - 1);
-        const int64_t row = (int64_t)tw.e * g.w.e_rows + (int64_t)c * g.w.row_mul +
-                            (up ? g.w.off_up : g.w.off_gate);
-        const void *base = up ? g.w.w_up : g.w.w_gate;
-        b_lr[i] = lr;
-        if (MX) {
-            b_ptr[i] = (const uint8_t *)base + row * (Kd / 2) + b_kc * 16;
-            s_ptr[i] = (up ? g.w.s_up : g.w.s_gate) + row * (Kd / 32) + b_kc;
-        } else {
-            b_ptr[i] = (const uint8_t *)base + (row * Kd + b_kc * 8) * 2;
-            s_ptr[i] = nullptr;
-        }
-    }
-
-    // h formats of this tile's rows (bf16 down GEMM): an fp16 h step is
-    // rounded to bf16 on its way into LDS
-    const uint8_t *hf = GATED ? nullptr : g.hfmt + (int64_t)tw.mg * g.h_tiles;
-    auto a_is_f16 = [&](int kt) -> bool {
-        return !GATED && !F16 && hf[(kt * TL::BK) / g.h_width] == kHF16;
-    };
-
-    u32x4 ra[TL::A_CH], rb[B_CH];
-    uint32_t rs[B_CH];
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-
-    auto gload = [&](int kt) {
-        const int k0 = kt * TL::BK;
-#pragma unroll
-        for (int i = 0; i < TL::A_CH; ++i)
-            ra[i] = (k0 + a_kc < Kd) ? *(const u32x4 *)(a_ptr[i] + k0) : zero4;
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            if (MX) {
-                const bool ok = k0 + b_kc * 32 < Kd;
-                rb[i] = ok ? *(const u32x4 *)(b_ptr[i] + k0 / 2) : zero4;
-                rs[i] = ok ? (uint32_t)s_ptr[i][k0 / 32] : 127u;
-            } else {
-                rb[i] = (k0 + b_kc * 8 < Kd) ? *(const u32x4 *)(b_ptr[i] + 2 * k0) : zero4;
-            }
-        }
-    };
-
-    auto lstore = [&](int st, bool a_f16) {
-        uint16_t *la = lds + st * TL::STAGE;
-        uint16_t *lb = la + TL::BM * TL::LDK;
-#pragma unroll
-        for (int i = 0; i < TL::A_CH; ++i) {
-            u32x4 v = ra[i];
-            if (a_f16) {
-#pragma unroll
-                for (int w = 0; w < 4; ++w) v[w] = f16x2_to_bf16x2(v[w]);
-            }
-            *(u32x4 *)(la + a_lr[i] * TL::LDK + a_kc) = v;
-        }
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            if (MX) {
-                decode_mxfp4<F16>(rb[i], e8m0_scale(rs[i]), lb + b_lr[i] * TL::LDK + b_kc * 32);
-            } else {
-                u32x4 v = rb[i];
-                if (F16) {
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) v[w] = bf16x2_to_f16x2(v[w]);
-                }
-                *(u32x4 *)(lb + b_lr[i] * TL::LDK + b_kc * 8) = v;
-            }
-        }
-    };
-
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wn = wave % TL::WN, wm = wave / TL::WN;
-    const int lrow = lane & 31, lk = (lane >> 5) * 8;
-
-    // LDS row of weight block f of this wave
-    auto brow = [&](int f) {
-        if (GATED)
-            return (f < TL::FN / 2) ? wn * (TL::TN / 2) + f * 32
-                                    : TL::BN / 2 + wn * (TL::TN / 2) + (f - TL::FN / 2) * 32;
-        return wn * TL::TN + f * 32;
-    };
-
-    f32x16 acc[TL::FN][TL::FM];
-#pragma unroll
-    for (int f = 0; f < TL::FN; ++f)
-#pragma unroll
-        for (int m = 0; m < TL::FM; ++m)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[f][m][r] = 0.0f;
-
-    auto compute = [&](int st) {
-        const uint16_t *la = lds + st * TL::STAGE;
-        const uint16_t *lb = la + TL::BM * TL::LDK;
-#pragma unroll
-        for (int ks = 0; ks < TL::BK / 16; ++ks) {
-            u32x4 bf[TL::FN], af[TL::FM];
-#pragma unroll
-            for (int f = 0; f < TL::FN; ++f)
-                bf[f] = *(const u32x4 *)(lb + (brow(f) + lrow) * TL::LDK + ks * 16 + lk);
-#pragma unroll
-            for (int m = 0; m < TL::FM; ++m)
-                af[m] = *(const u32x4 *)(la + (wm * TL::TM + m * 32 + lrow) * TL::LDK +
-                                         ks * 16 + lk);
-#pragma unroll
-            for (int f = 0; f < TL::FN; ++f)
-#pragma unroll
-                for (int m = 0; m < TL::FM; ++m)
-                    acc[f][m] = mfma<F16>(bf[f], af[m], acc[f][m]);
-        }
-    };
-
-    const int nk = (Kd + TL::BK - 1) / TL::BK;
-    gload(0);
-    lstore(0, a_is_f16(0));
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) gload(kt + 1);
-        compute(cur);
-        if (more) lstore(cur ^ 1, a_is_f16(kt + 1));
-        __syncthreads();
-    }
-
-    epilogue<TL, GATED>(g, tw, acc, s_red);
-}
-
-template <class TL, bool MX, bool GATED>
-__global__ __launch_bounds__(TL::NT) void gemm_kernel(GemmArgs g)
-{
-    constexpr int NW = GATED ? TL::BN / 2 : TL::BN;   // output features per tile
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * TL::STAGE];
-    __shared__ int s_cum[kMaxExperts + 1];
-    __shared__ float s_red[TL::NT / 64];
-
-    TileWork tw;
-    if (!find_tile(g, s_cum, TL::BM, NW, &tw)) return;
-    if (GATED) {
-        gemm_body<TL, MX, GATED, false>(g, tw, lds, s_red);
-        return;
-    }
-    // down GEMM: fp16 operands iff every h tile of these rows is fp16
-    const uint8_t *hf = g.hfmt + (int64_t)tw.mg * g.h_tiles;
-    int all16 = g.f16_ok;
-    for (int i = threadIdx.x; i < g.h_tiles; i += TL::NT) all16 &= hf[i] == kHF16;
-    if (__syncthreads_and(all16)) gemm_body<TL, MX, GATED, true>(g, tw, lds, s_red);
-    else gemm_body<TL, MX, GATED, false>(g, tw, lds, s_red);
-}
-
-template <class TL, bool MX, bool GATED>
-hipError_t launch(const GemmArgs &a, int64_t max_m_tiles, hipStream_t s)
-{
-    const int64_t grid = max_m_tiles * a.nN + 8;
-    gemm_kernel<TL, MX, GATED><<<dim3((unsigned)grid), dim3(TL::NT), 0, s>>>(a);
-    return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
-// Pipelined kernel for 16-bit weights: gfx950 direct global->LDS loads.
+// Pipelined kernel: gfx950 direct global->LDS loads.
 //
-// Each k-step's A and B panels are fetched by global_load_lds_dwordx4 (16 bytes
-// per lane straight into LDS, no staging registers) into one of S LDS stages;
-// S-1 k-steps are in flight while one is computed.  One barrier per k-step,
+// Each k-step's token and weight panels are fetched by global_load_lds_dwordx4
+// (16 bytes per lane straight into LDS, no staging registers) into one of
+// SA (tokens) / SB (weights) LDS stages; the next token step and SB-1 weight
+// steps are in flight while one is computed.  One barrier per k-step,
 // preceded by a wait for this thread's own loads of the step about to be read.
-// LDS rows are BK*2 bytes; the 16-byte chunk c of row r sits at physical chunk
-// c ^ sw(r).  gfx950 serves a 16-byte-per-lane LDS read 16 lanes at a time
-// across 64 four-byte banks (measured: this swizzle has no bank conflicts,
-// one built for 8 lanes / 32 banks had a conflict on half the LDS cycles), so
-// the 16 lanes that read one chunk column of 16 consecutive rows must land in
-// 16 different 16-byte bank groups.  Each load instruction of a wave fills
-// one contiguous KiB of LDS; the swizzle is applied by choosing which global
-// chunk each lane fetches.
+//
+// 16-bit LDS rows are BK*2 bytes; the 16-byte chunk c of row r sits at
+// physical chunk c ^ sw(r).  gfx950 serves a 16-byte-per-lane LDS read 16
+// lanes at a time across 64 four-byte banks (measured: this swizzle has no
+// bank conflicts, one built for 8 lanes / 32 banks had a conflict on half the
+// LDS cycles), so the 16 lanes that read one chunk column of 16 consecutive
+// rows must land in 16 different 16-byte bank groups.  Each load instruction
+// of a wave fills one contiguous KiB of LDS; the swizzle is applied by
+// choosing which global chunk each lane fetches.
+//
+// MXFP4 weight stages hold the packed layout unchanged: per 32-row block one
+// KiB of codes (32 bytes a row, halves swapped on bit 3 of the row: the 16
+// lanes of a read hit 64 distinct banks) and 64 bytes of scales.  A k-step
+// of 64 is consumed in a permuted k order that both operands share: MFMA
+// sub-step s, lane half h covers k = 32h + 8s .. 32h + 8s + 7 (instead of
+// 16s + 8h ..).  A lane's weight codes for the whole k-step are then one
+// 16-byte LDS read and lie in one scale block (h).
 //
 // Operand conversion happens after the LDS read, in registers: fp16 down GEMM
 // steps convert the bf16 weight fragments to fp16 (exact, range checked at
-// prepare); bf16 down GEMM steps round fp16-stored h fragments to bf16.
-// A ragged last k-step loads clamped in-row addresses and zeroes the operand
-// fragments past the reduction length.
+// prepare) or decode MXFP4 to fp16; bf16 down GEMM steps round fp16-stored h
+// fragments to bf16.  Token chunks past the reduction length are read from a
+// zero buffer; packed MXFP4 weights are zero past it already.
 
-template <int BN_, int BM_, int BK_, int WN_, int WM_, int SA_, int SB_>
+template <int BN_, int BM_, int BK_, int WN_, int WM_, int SA_, int SB_, bool MX_>
 struct DTile {
     static constexpr int BN = BN_, BM = BM_, BK = BK_, WN = WN_, WM = WM_;
     static constexpr int SA = SA_, SB = SB_;            // LDS stages of A and of B
+    static constexpr bool MX = MX_;                     // MXFP4 weights (packed)
     static constexpr int NT = 64 * WN * WM;
     static constexpr int NWAVES = WN * WM;
     static constexpr int TN = BN / WN, TM = BM / WM;
     static constexpr int FN = TN / 32, FM = TM / 32;
-    static constexpr int CPR = BK / 8;                  // 16-byte chunks per row
-    static constexpr int ROWB = BK * 2;                 // bytes per LDS row
-    static constexpr int NA = BM * CPR / NT;            // A loads per thread per step
-    static constexpr int NB = BN * CPR / NT;            // B loads per thread per step
-    static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+    static constexpr int CPR = BK / 8;                  // 16-byte chunks per token row
+    static constexpr int ROWB = BK * 2;                 // bytes per token row
+    static constexpr int NA = BM * CPR / NT;            // token loads per thread per step
+    // weights: 16-bit rows like the tokens, or MXFP4 KiB code blocks plus one
+    // scale load (RBW row-blocks of 64 bytes per wave)
+    static constexpr int RB = BN / 32;                  // 32-row weight blocks
+    static constexpr int RBW = RB / NWAVES;             // scale pieces per wave (MXFP4)
+    static constexpr int NBC = MX ? RB / NWAVES : BN * CPR / NT;   // weight-row loads
+    static constexpr int NB = MX ? NBC + 1 : NBC;       // weight loads per thread per step
+    static constexpr int CODE_BYTES = BN * BK / 2;      // MXFP4 codes of a stage
+    static constexpr int A_BYTES = BM * ROWB;
+    static constexpr int B_BYTES = MX ? CODE_BYTES + RB * 64 : BN * ROWB;
     static constexpr int B_BASE = SA * A_BYTES;         // B stages follow the A stages
     static constexpr int LDS_BYTES = SA * A_BYTES + SB * B_BYTES;
-    static_assert(NA * NT == BM * CPR && NB * NT == BN * CPR, "whole loads per thread");
-    static_assert(NA >= 1 && NB >= 1, "every thread loads A and B");
+    static_assert(NA * NT == BM * CPR, "whole token loads per thread");
+    static_assert(MX ? (RBW * NWAVES == RB && RBW >= 1 && BK == 64)
+                     : (NBC * NT == BN * CPR), "whole weight loads per thread");
+    static_assert(NA >= 1 && NBC >= 1, "every thread loads A and B");
     static_assert(FN >= 2 && FN % 2 == 0, "gate/up pairs per wave");
     static_assert(SA == 2 && SB >= SA && SB <= 4, "A one step ahead, B up to three");
     static_assert(2 * NB <= 63, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(B_BYTES % 1024 == 0 || MX, "KiB-aligned stages");
     static_assert(LDS_BYTES >= (kMaxExperts + 1) * 4 && LDS_BYTES >= NWAVES * 4,
                   "scheduling table and epilogue scratch overlay the stages");
-    // swizzle of row r: rows r and r + 16/CPR start in the same bank group
+    // swizzle of token row r: rows r and r + 16/CPR start in the same bank group
     __device__ static inline int sw(int r) { return (r / (16 / CPR)) % CPR; }
     static_assert(CPR == 4 || CPR == 8 || CPR == 16, "row of 64, 128 or 256 bytes");
 };
@@ -482,9 +287,19 @@ struct DTile {
 // 512 threads, wave 64x128; k-steps of 64 (128-byte rows: a 64-byte row
 // piece halves the L2->LDS rate); A (token rows, L2/MALL resident) two
 // stages, B (weights, first touch from HBM) three: 2 x 32 + 3 x 32 KiB.
-using PrefillDTile = DTile<256, 256, 64, 4, 2, 2, 3>;
+using PrefillDTile = DTile<256, 256, 64, 4, 2, 2, 3, false>;
 // 256 threads, wave 64x32; weights stream from HBM: four B stages.
-using DecodeDTile = DTile<256, 32, 64, 4, 1, 2, 4>;
+using DecodeDTile = DTile<256, 32, 64, 4, 1, 2, 4, false>;
+// MXFP4 weights: a weight stage is 8.5 KiB, so four of them fit beside the
+// token stages (2 x 32 + 4 x 8.5 KiB; decode 2 x 4 + 4 x 8.5 KiB).
+using PrefillMXTile = DTile<256, 256, 64, 4, 2, 2, 4, true>;
+using DecodeMXTile = DTile<256, 32, 64, 4, 1, 2, 4, true>;
+// Mid tiles, 256 x 128 rows, for experts of a few hundred rows (a 256-row
+// tile would run a mostly empty second tile per expert).  16-bit: 512
+// threads, wave 64x64, 2 x 16 + 3 x 32 KiB.  MXFP4: 256 threads, wave
+// 64x128, 2 x 16 + 4 x 8.5 KiB, so two workgroups share a CU.
+using MidDTile = DTile<256, 128, 64, 4, 2, 2, 3, false>;
+using MidMXTile = DTile<256, 128, 64, 4, 1, 2, 4, true>;
 
 // 16 bytes per lane from global memory straight into LDS: lane l writes
 // LDS bytes [m0 + 16 l, m0 + 16 l + 16).  Issued as inline asm so that the
@@ -513,7 +328,7 @@ __device__ __forceinline__ void wait_loads_barrier()
 __device__ const u32x4 g_zero16 = {0u, 0u, 0u, 0u};
 
 // RAGGED: the reduction length is not a multiple of BK (the last k-step's
-// chunks past it read zeros); otherwise no k-step needs a bounds test.
+// token chunks past it read zeros); otherwise no k-step needs a bounds test.
 template <class TL, bool GATED, bool F16, bool RAGGED>
 __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, uint8_t *lds,
                                          float *s_red)
@@ -521,7 +336,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Kd = g.Kd;
 
-    // ---- per-load global sources: row base + swizzled chunk
+    // ---- per-load global sources of the token rows: row base + swizzled chunk
     const uint8_t *a_src[TL::NA];
     int a_k[TL::NA];                   // first k of the chunk this load fetches
 #pragma unroll
@@ -534,44 +349,83 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
         a_k[i] = c * 8;
         a_src[i] = (const uint8_t *)g.a + ((int64_t)src * Kd + c * 8) * 2;
     }
-    const uint8_t *b_src[TL::NB];
-    int b_k[TL::NB];
+    // ---- weight sources.  16-bit: row base + swizzled chunk.  MXFP4: this
+    // lane's 16 bytes of the KiB code block of tile row-block t (load i), and
+    // of the 64-byte scale piece of row-block RBW * wave + lane / 4.
+    const uint8_t *b_src[TL::NBC];
+    int b_k[TL::NBC];
+    const uint8_t *s_src = nullptr;
+    if constexpr (TL::MX) {
+        // logical row-block (packed layout) of tile row-block t
+        const int nrb_tot = (GATED ? 2 : 1) * g.nrb_half;
+        auto lrb = [&](int t) {
+            const bool up = GATED && t >= TL::RB / 2;
+            const int tt = up ? t - TL::RB / 2 : t;
+            return (up ? g.nrb_half : 0) + min(tw.n0 / 32 + tt, g.nrb_half - 1);
+        };
 #pragma unroll
-    for (int i = 0; i < TL::NB; ++i) {
-        const int q = (i * TL::NWAVES + wave) * 64 + lane;
-        const int row = q / TL::CPR, p = q % TL::CPR;
-        const int c = p ^ TL::sw(row);
-        const bool up = GATED && row >= TL::BN / 2;
-        const int f = min(tw.n0 + (up ? row - TL::BN / 2 : row), g.Nout - 1);
-        const int64_t wrow = (int64_t)tw.e * g.w.e_rows + (int64_t)f * g.w.row_mul +
-                             (up ? g.w.off_up : g.w.off_gate);
-        const void *base = up ? g.w.w_up : g.w.w_gate;
-        b_k[i] = c * 8;
-        b_src[i] = (const uint8_t *)base + (wrow * Kd + c * 8) * 2;
+        for (int i = 0; i < TL::NBC; ++i) {
+            const int t = i * TL::NWAVES + wave;
+            b_k[i] = 0;
+            b_src[i] = g.pk + ((int64_t)tw.e * nrb_tot + lrb(t)) * g.nks * 1024 + lane * 16;
+        }
+        const int t = wave * TL::RBW + min(lane / 4, TL::RBW - 1);
+        s_src = g.pks + ((int64_t)tw.e * nrb_tot + lrb(t)) * g.nks * 64 + (lane % 4) * 16;
+    } else {
+#pragma unroll
+        for (int i = 0; i < TL::NBC; ++i) {
+            const int q = (i * TL::NWAVES + wave) * 64 + lane;
+            const int row = q / TL::CPR, p = q % TL::CPR;
+            const int c = p ^ TL::sw(row);
+            const bool up = GATED && row >= TL::BN / 2;
+            const int f = min(tw.n0 + (up ? row - TL::BN / 2 : row), g.Nout - 1);
+            const int64_t wrow = (int64_t)tw.e * g.w.e_rows + (int64_t)f * g.w.row_mul +
+                                 (up ? g.w.off_up : g.w.off_gate);
+            const void *base = up ? g.w.w_up : g.w.w_gate;
+            b_k[i] = c * 8;
+            b_src[i] = (const uint8_t *)base + (wrow * Kd + c * 8) * 2;
+        }
     }
     const uint8_t *zero = (const uint8_t *)&g_zero16;
 
-    // LDS byte offset of this wave's first KiB of a stage (wave-uniform)
+    // LDS byte offset of this wave's first KiB of a stage, and of its scale
+    // pieces (wave-uniform)
     const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds_offset(lds) + wave * 1024);
+    const uint32_t wave_sc = __builtin_amdgcn_readfirstlane(
+        lds_offset(lds) + TL::B_BASE + TL::CODE_BYTES + wave * TL::RBW * 64);
     const int nk = (Kd + TL::BK - 1) / TL::BK;
     const int nfull = RAGGED ? Kd / TL::BK : nk;    // k-steps with no chunk past Kd
-    auto issue_a = [&](int kt) {
+    auto issue_a_one = [&](int kt, int i) {
         const uint32_t st = wave_lds + (kt % TL::SA) * TL::A_BYTES;
         const int k0 = kt * TL::BK;
         const bool full = kt < nfull;
-#pragma unroll
-        for (int i = 0; i < TL::NA; ++i)
-            dma16((!RAGGED || full || k0 + a_k[i] < Kd) ? a_src[i] + 2 * k0 : zero,
-                  st + i * TL::NWAVES * 1024);
+        dma16((!RAGGED || full || k0 + a_k[i] < Kd) ? a_src[i] + 2 * k0 : zero,
+              st + i * TL::NWAVES * 1024);
     };
-    auto issue_b = [&](int kt) {
-        const uint32_t st = wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
-        const int k0 = kt * TL::BK;
-        const bool full = kt < nfull;
-#pragma unroll
-        for (int i = 0; i < TL::NB; ++i)
+    // weight load i of step kt (MXFP4: i == NBC is the scale load)
+    auto issue_b_one = [&](int kt, int i) {
+        if constexpr (TL::MX) {
+            if (i < TL::NBC) {
+                dma16(b_src[i] + (int64_t)kt * 1024,
+                      wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES + i * TL::NWAVES * 1024);
+            } else if (lane < 4 * TL::RBW) {
+                dma16(s_src + (int64_t)kt * 64, wave_sc + (kt % TL::SB) * TL::B_BYTES);
+            }
+        } else {
+            const uint32_t st = wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
+            const int k0 = kt * TL::BK;
+            const bool full = kt < nfull;
             dma16((!RAGGED || full || k0 + b_k[i] < Kd) ? b_src[i] + 2 * k0 : zero,
                   st + i * TL::NWAVES * 1024);
+        }
+    };
+    auto issue_a = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < TL::NA; ++i) issue_a_one(kt, i);
+    };
+    auto issue_b = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < TL::NB; ++i) issue_b_one(kt, i);
     };
 
     // ---- fragment addressing (row r of a 32-row block = lane % 32)
@@ -584,6 +438,9 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
                                     : TL::BN / 2 + wn * (TL::TN / 2) + (f - TL::FN / 2) * 32;
         return wn * TL::TN + f * 32;
     };
+    // MXFP4: this lane's code chunk within a row-block's KiB, and scale byte
+    const int mx_code = lrow * 32 + 16 * (lhalf ^ ((lrow >> 3) & 1));
+    const int mx_scale = lhalf * 32 + lrow;
 
     // h formats of these rows (bf16 down GEMM only; read from global memory,
     // whose waits only ever lengthen the explicit ones)
@@ -605,24 +462,41 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     auto kloop = [&](auto mv_tag) {
         constexpr int MV = decltype(mv_tag)::value;
         u32x4 bf[2][TL::FN], af[2][TL::FM > 0 ? TL::FM : 1];
+        u32x4 cq[TL::MX ? TL::FN : 1];     // MXFP4 codes of the current k-step
+        float scf[TL::MX ? TL::FN : 1];    // and their scale multipliers
         // read the fragments of sub-step ks of k-step kt into buffer b
         auto read = [&](int kt, int ks, int b) {
             const uint8_t *sa = lds + (kt % TL::SA) * TL::A_BYTES;
             const uint8_t *sb = lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
-            const int coff = ((ks * 2 + lhalf) ^ lsw) * 16;
+            if constexpr (TL::MX) {
+                if (ks == 0) {
+#pragma unroll
+                    for (int f = 0; f < TL::FN; ++f) {
+                        const int t = brow(f) / 32;
+                        cq[f] = *(const u32x4 *)(sb + t * 1024 + mx_code);
+                        scf[f] = e8m0_scale(sb[TL::CODE_BYTES + t * 64 + mx_scale]);
+                    }
+                }
+#pragma unroll
+                for (int f = 0; f < TL::FN; ++f) bf[b][f] = decode_mxfp4_8<F16>(cq[f][ks], scf[f]);
+            } else {
+                const int coff = ((ks * 2 + lhalf) ^ lsw) * 16;
+#pragma unroll
+                for (int f = 0; f < TL::FN; ++f) {
+                    bf[b][f] = *(const u32x4 *)(sb + (brow(f) + lrow) * TL::ROWB + coff);
+                    if (F16) {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) bf[b][f][w] = bf16x2_to_f16x2(bf[b][f][w]);
+                    }
+                }
+            }
+            // token chunk of this sub-step (MXFP4: the permuted k order)
+            const int acoff = ((TL::MX ? 4 * lhalf + ks : ks * 2 + lhalf) ^ lsw) * 16;
             // bf16 down GEMM: an fp16-stored h step is rounded to bf16
             const bool a_f16 = !GATED && !F16 && hf[(kt * TL::BK) / g.h_width] == kHF16;
 #pragma unroll
-            for (int f = 0; f < TL::FN; ++f) {
-                bf[b][f] = *(const u32x4 *)(sb + (brow(f) + lrow) * TL::ROWB + coff);
-                if (F16) {
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) bf[b][f][w] = bf16x2_to_f16x2(bf[b][f][w]);
-                }
-            }
-#pragma unroll
             for (int m = 0; m < MV; ++m) {
-                af[b][m] = *(const u32x4 *)(sa + (wm * TL::TM + m * 32 + lrow) * TL::ROWB + coff);
+                af[b][m] = *(const u32x4 *)(sa + (wm * TL::TM + m * 32 + lrow) * TL::ROWB + acoff);
                 if (a_f16) {
 #pragma unroll
                     for (int w = 0; w < 4; ++w) af[b][m][w] = f16x2_to_bf16x2(af[b][m][w]);
@@ -652,23 +526,13 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
         // order of issue, which the waits rely on, is unchanged
         auto issue_group_part = [&](int j, int part) {
             constexpr int L = TL::NA + TL::NB;
-            const uint32_t sta = wave_lds + ((j + 1) % TL::SA) * TL::A_BYTES;
-            const uint32_t stb = wave_lds + TL::B_BASE + ((j + TL::SB - 1) % TL::SB) * TL::B_BYTES;
-            const int ka = (j + 1) * TL::BK, kb = (j + TL::SB - 1) * TL::BK;
-            const bool fa = j + 1 < nfull, fb = j + TL::SB - 1 < nfull;
 #pragma unroll
             for (int q = 0; q < L; ++q) {
                 if (q < part * L / NKS || q >= (part + 1) * L / NKS) continue;
                 if (q < TL::NA) {
-                    const int i = q;
-                    if (j + 1 < nk)
-                        dma16((!RAGGED || fa || ka + a_k[i] < Kd) ? a_src[i] + 2 * ka : zero,
-                              sta + i * TL::NWAVES * 1024);
+                    if (j + 1 < nk) issue_a_one(j + 1, q);
                 } else {
-                    const int i = q - TL::NA;
-                    if (j + TL::SB - 1 < nk)
-                        dma16((!RAGGED || fb || kb + b_k[i] < Kd) ? b_src[i] + 2 * kb : zero,
-                              stb + i * TL::NWAVES * 1024);
+                    if (j + TL::SB - 1 < nk) issue_b_one(j + TL::SB - 1, q - TL::NA);
                 }
             }
         };
@@ -720,8 +584,10 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     epilogue<TL, GATED>(g, tw, acc, s_red);
 }
 
+// At least two waves per SIMD (256 VGPRs each): the 4-wave MXFP4 mid tile
+// then runs two workgroups per CU.
 template <class TL, bool GATED>
-__global__ __launch_bounds__(TL::NT) void gemm_dma_kernel(GemmArgs g)
+__global__ __launch_bounds__(TL::NT, 2) void gemm_dma_kernel(GemmArgs g)
 {
     constexpr int NW = GATED ? TL::BN / 2 : TL::BN;
     // one LDS allocation: the scheduling table, then the stages, then the
@@ -803,24 +669,72 @@ __global__ __launch_bounds__(256) void weight_range_kernel(const uint32_t *w, co
     }
 }
 
+// ---- prepare-time repack of an MXFP4 stack (layout: PackArgs).  Thread i
+// writes packed code chunk i (16 bytes) and packed scale byte i.
+__global__ __launch_bounds__(256) void mx_pack_kernel(PackArgs a)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int rbh = a.Nh / 32;                       // row-blocks per operand
+    const int64_t nrb = (int64_t)a.ops * rbh;
+    const int64_t total = (int64_t)a.E * nrb * a.nks * 64;
+    if (i >= total) return;
+    const int kq = a.K / 2, ksc = a.K / 32;          // code / scale bytes per row
+    {
+        // code chunk: (e, lb, ks, r, p)
+        const int p = (int)(i & 1), r = (int)((i >> 1) & 31);
+        const int64_t blk = i >> 6;                  // (e, lb, ks)
+        const int ks = (int)(blk % a.nks);
+        const int64_t elb = blk / a.nks;
+        const int lb = (int)(elb % nrb), e = (int)(elb / nrb);
+        const int op = lb / rbh, f = (lb % rbh) * 32 + r;
+        const int c = p ^ ((r >> 3) & 1);           // logical half stored here
+        const int64_t row = (int64_t)e * a.e_rows + (int64_t)f * a.row_mul + a.off[op];
+        const int kb = ks * 32 + 16 * c;             // first code byte
+        uint8_t v[16];
+        const uint8_t *src = a.codes[op] + row * kq + kb;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = kb + j < kq ? src[j] : 0;
+        uint8_t *dst = a.pk + i * 16;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dst[j] = v[j];
+    }
+    {
+        // scale byte: (e, lb, ks, h, r)
+        const int r = (int)(i & 31), h = (int)((i >> 5) & 1);
+        const int64_t blk = i >> 6;
+        const int ks = (int)(blk % a.nks);
+        const int64_t elb = blk / a.nks;
+        const int lb = (int)(elb % nrb), e = (int)(elb / nrb);
+        const int op = lb / rbh, f = (lb % rbh) * 32 + r;
+        const int64_t row = (int64_t)e * a.e_rows + (int64_t)f * a.row_mul + a.off[op];
+        const int sbk = ks * 2 + h;
+        a.pks[i] = sbk < ksc ? a.scales[op][row * ksc + sbk] : (uint8_t)127;
+    }
+}
+
 }  // namespace
 
-// The MXFP4 (register-staged) and 16-bit (DMA) kernels of one variant share
-// their tile shape, which the host uses for scheduling and the h formats.
-static_assert(PrefillTile::BM == PrefillDTile::BM && PrefillTile::BN == PrefillDTile::BN, "");
-static_assert(DecodeTile::BM == DecodeDTile::BM && DecodeTile::BN == DecodeDTile::BN, "");
-static_assert((PrefillTile::BN / 2) % PrefillDTile::BK == 0 && (DecodeTile::BN / 2) % DecodeDTile::BK == 0 &&
-              (PrefillTile::BN / 2) % PrefillTile::BK == 0 && (DecodeTile::BN / 2) % DecodeTile::BK == 0,
+// The MXFP4 and 16-bit kernels of one variant share their tile shape, which
+// the host uses for scheduling and the h formats.
+static_assert(PrefillMXTile::BM == PrefillDTile::BM && PrefillMXTile::BN == PrefillDTile::BN, "");
+static_assert(DecodeMXTile::BM == DecodeDTile::BM && DecodeMXTile::BN == DecodeDTile::BN, "");
+static_assert(MidMXTile::BM == MidDTile::BM && MidMXTile::BN == MidDTile::BN, "");
+static_assert((PrefillDTile::BN / 2) % PrefillDTile::BK == 0 &&
+              (DecodeDTile::BN / 2) % DecodeDTile::BK == 0,
               "a down-GEMM k-step lies inside one h tile");
 
 int gemm_bm(GemmKind kind)
 {
-    return kind == GemmKind::kPrefill ? PrefillTile::BM : DecodeTile::BM;
+    return kind == GemmKind::kPrefill ? PrefillDTile::BM
+           : kind == GemmKind::kMid   ? MidDTile::BM
+                                      : DecodeDTile::BM;
 }
 
 int gemm_bn(GemmKind kind, bool gated)
 {
-    const int bn = kind == GemmKind::kPrefill ? PrefillTile::BN : DecodeTile::BN;
+    const int bn = kind == GemmKind::kPrefill ? PrefillDTile::BN
+                   : kind == GemmKind::kMid   ? MidDTile::BN
+                                              : DecodeDTile::BN;
     return gated ? bn / 2 : bn;
 }
 
@@ -829,16 +743,35 @@ hipError_t launch_gemm_bf16(GemmKind kind, bool gated, bool mxfp4, const GemmArg
 {
     if (kind == GemmKind::kPrefill) {
         if (mxfp4)
-            return gated ? launch<PrefillTile, true, true>(a, max_m_tiles, s)
-                         : launch<PrefillTile, true, false>(a, max_m_tiles, s);
+            return gated ? launch_dma<PrefillMXTile, true>(a, max_m_tiles, s)
+                         : launch_dma<PrefillMXTile, false>(a, max_m_tiles, s);
         return gated ? launch_dma<PrefillDTile, true>(a, max_m_tiles, s)
                      : launch_dma<PrefillDTile, false>(a, max_m_tiles, s);
     }
+    if (kind == GemmKind::kMid) {
+        if (mxfp4)
+            return gated ? launch_dma<MidMXTile, true>(a, max_m_tiles, s)
+                         : launch_dma<MidMXTile, false>(a, max_m_tiles, s);
+        return gated ? launch_dma<MidDTile, true>(a, max_m_tiles, s)
+                     : launch_dma<MidDTile, false>(a, max_m_tiles, s);
+    }
     if (mxfp4)
-        return gated ? launch<DecodeTile, true, true>(a, max_m_tiles, s)
-                     : launch<DecodeTile, true, false>(a, max_m_tiles, s);
+        return gated ? launch_dma<DecodeMXTile, true>(a, max_m_tiles, s)
+                     : launch_dma<DecodeMXTile, false>(a, max_m_tiles, s);
     return gated ? launch_dma<DecodeDTile, true>(a, max_m_tiles, s)
                  : launch_dma<DecodeDTile, false>(a, max_m_tiles, s);
+}
+
+hipError_t launch_mx_pack(const PackArgs &a, hipStream_t s)
+{
+    const int64_t nrb = (int64_t)a.ops * (a.Nh / 32);
+    const int64_t chunks = (int64_t)a.E * nrb * a.nks * 64;     // 16-byte code chunks
+    const int64_t sbytes = (int64_t)a.E * nrb * a.nks * 64;     // scale bytes
+    const int64_t n = chunks > sbytes ? chunks : sbytes;
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    mx_pack_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_weight_range(const void *w, const uint8_t *scales, int64_t n_words,

@@ -78,7 +78,47 @@ struct GemmArgs {
     int h_tiles;                 // GEMM-1 feature tiles (row stride of hfmt)
     int h_width;                 // h columns per GEMM-1 feature tile
     int f16_ok;                  // the down weights convert exactly to fp16
+    // MXFP4 weights, packed once at prepare (see PackArgs): codes and scales
+    // of logical row-block lb, k-step ks at pk + (lb-major) KiB blocks
+    const uint8_t *pk;           // [E][nrb][nks][32 rows][32 bytes]
+    const uint8_t *pks;          // [E][nrb][nks][2 scale blocks][32 rows]
+    int nks;                     // k-steps of 64 (the reduction length, rounded up)
+    int nrb_half;                // row-blocks of one operand (Nout / 32)
 };
+
+// Prepare-time repack of an MXFP4 weight stack into the layout the GEMM
+// streams.  Logical rows: operand 0 (gate, or the only operand) then operand
+// 1 (up), Nh rows each; logical row f of operand o lives at stack row
+// e * e_rows + f * row_mul + off[o].  For row-block lb (32 rows) and k-step ks
+// (64 elements) the packed codes are one KiB: row r's 32 code bytes at
+// r * 32, its two 16-byte halves swapped when bit 3 of r is set (the LDS
+// bank swizzle, applied here so the GEMM copies whole KiB blocks); the packed
+// scales are 64 bytes: [scale block 0..1][row 0..31].  Past the reduction
+// length codes are 0 (+0.0) and scale bytes 127 (1.0).
+struct PackArgs {
+    const uint8_t *codes[2];     // [.., K/2] per stack row
+    const uint8_t *scales[2];    // [.., K/32] per stack row
+    int64_t e_rows;
+    int row_mul;
+    int off[2];
+    int ops;                     // 2 (gate, up) or 1
+    int Nh;                      // rows per operand
+    int K;                       // reduction length (multiple of 32)
+    int nks;                     // ceil(K / 64)
+    int E;
+    uint8_t *pk;
+    uint8_t *pks;
+};
+hipError_t launch_mx_pack(const PackArgs &a, hipStream_t s);
+// bytes of the packed codes / scales of an MXFP4 stack
+inline int64_t mx_pack_bytes(int ops, int64_t Nh, int64_t K, int64_t E)
+{
+    return E * (ops * Nh / 32) * ((K + 63) / 64) * 1024;
+}
+inline int64_t mx_pack_scale_bytes(int ops, int64_t Nh, int64_t K, int64_t E)
+{
+    return E * (ops * Nh / 32) * ((K + 63) / 64) * 64;
+}
 
 // Range of a down-weight stack, for the choice of the fp16 down GEMM:
 // out[0] = max over elements of the bf16 magnitude bits (0x7f80 = inf),
@@ -103,8 +143,9 @@ hipError_t launch_permute(const PermuteArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
 // Grouped-GEMM variants.  `gated` selects the gate||up GEMM with the fused
-// activation (bf16 h out) versus the down GEMM (+bias, f32 y out).
-enum class GemmKind { kPrefill = 0, kDecode = 1 };
+// activation (16-bit h out) versus the down GEMM (+bias, f32 y out).  With
+// mxfp4 the weights are read from the packed copy (GemmArgs pk / pks).
+enum class GemmKind { kPrefill = 0, kDecode = 1, kMid = 2 };
 int gemm_bm(GemmKind kind);          // token-tile height of a variant
 int gemm_bn(GemmKind kind, bool gated);   // output features per tile
 hipError_t launch_gemm_bf16(GemmKind kind, bool gated, bool mxfp4,

@@ -67,7 +67,8 @@ def create(L, E=8, H=64, I=32, K=2, dtype="bf16", gub=False, db=False, **opt):
     dict(H=60), dict(dtype="mxfp4", H=48), dict(n_group=3, topk_group=1),
     dict(n_group=4, topk_group=5), dict(n_group=4, topk_group=1, K=3),
     dict(n_group=128, E=256, topk_group=1, K=1), dict(scoring=7),
-    dict(activation=5), dict(swiglu_fusion=3)])
+    dict(activation=5), dict(swiglu_fusion=3), dict(gemm_variant=4),
+    dict(gemm_variant=-1)])
 def test_create_rejects_bad_geometry(L, kw):
     st, h = create(L, **kw)
     assert st == 1, L.lib().moe_last_error()

@@ -26,7 +26,7 @@ def oracle_full(cfg, inp, T=None):
 # ------------------------------------------------------------------ small sizes
 
 @pytest.mark.parametrize("name", synth.SMALL_CONFIGS)
-@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
 def test_small_configs_elementwise(name, variant):
     """Every output element of the five workloads at oracle-sized shapes, with
     the kernel choice automatic, forced large-M, and forced small-M."""
@@ -42,12 +42,12 @@ def test_small_configs_elementwise(name, variant):
 
 @pytest.mark.parametrize("layout", ["split", "interleaved", "unfused"])
 @pytest.mark.parametrize("w_dtype", ["bf16", "mxfp4", "f32"])
-@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("variant", [1, 2, 3])
 def test_layouts_dtypes_biases(layout, w_dtype, variant):
     """Each gate||up layout with each weight type, expert biases on, ragged
     token count and feature tails."""
     x_dtype = "f32" if w_dtype == "f32" else "bf16"
-    if w_dtype == "f32" and variant == 2:
+    if w_dtype == "f32" and variant >= 2:
         pytest.skip("f32 layers have one kernel")
     cfg = synth.MoeConfig(name="lay", cid=201, T=333, H=352, I=224, E=6, K=2,
                           x_dtype=x_dtype, w_dtype=w_dtype, layout=layout,
@@ -108,7 +108,7 @@ def test_routing_modes_bf16(routing):
     compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"routing bf16 {routing}")
 
 
-@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("variant", [1, 2, 3])
 def test_h_overflow_falls_back_to_bf16(variant):
     """h beyond fp16's range in some tiles: those tiles are stored in bf16 and
     the down GEMM of their rows runs in bf16 (fp16 tiles rounded to bf16)."""
@@ -142,7 +142,7 @@ def test_zero_tokens():
     assert out.shape == (0, cfg.H)
 
 
-@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("variant", [1, 2, 3])
 def test_all_tokens_on_one_expert(variant):
     """A fully skewed load: one expert holds every token's first slot, many
     experts are empty (zero-row experts launch no tiles)."""
