@@ -21,6 +21,7 @@ reduction dimension.
 from __future__ import annotations
 
 import dataclasses
+import math
 import hashlib
 from typing import Dict, Optional
 
@@ -28,7 +29,10 @@ import torch
 
 # tensor ids used in seeds
 T_X, T_LOGITS, T_GATE_UP, T_UP, T_DOWN, T_GU_BIAS, T_DOWN_BIAS, T_SEL_BIAS, \
-    T_GATE_BIAS, T_SHARED = range(10)
+    T_GATE_BIAS, T_SHARED, T_ROUTER_W, T_ROUTER_B = range(12)
+
+# activations that read a gate and an up projection (the others read one)
+GATED_ACTS = ("silu", "swiglu_clamped")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -57,14 +61,22 @@ class MoeConfig:
     selection_bias_std: Optional[float] = None   # e_score_correction_bias [E]
     logit_std: float = 1.0
     shared_output: bool = False   # draw a [T,H] shared-expert output
+    gelu_mode: str = "erf"        # "erf" | "tanh" (activation "gelu")
+    weigh_inputs: bool = False    # kept weight scales the expert's input
+    router: bool = False          # draw router_weight [H,E] and router_bias [E]
 
     def replace(self, **kw) -> "MoeConfig":
         return dataclasses.replace(self, **kw)
 
     @property
+    def gated(self) -> bool:
+        return self.activation in GATED_ACTS
+
+    @property
     def flops(self) -> int:
-        """Active multiply-add flops of the gated expert FFN: 6*T*K*H*I."""
-        return 6 * self.T * self.K * self.H * self.I
+        """Active multiply-add flops of the expert FFNs: 6*T*K*H*I gated,
+        4*T*K*H*I with one fc1 projection (router not counted)."""
+        return (6 if self.gated else 4) * self.T * self.K * self.H * self.I
 
 
 # The five workloads.  Full sizes are the measured shapes; the "_small"
@@ -183,28 +195,30 @@ def make_inputs(cfg: MoeConfig, device="cpu", T: Optional[int] = None) -> dict:
     out["x"] = normal((T, H), 1.0, xd, dev, seed_of(cid, T_X))
     out["logits"] = normal((T, E), cfg.logit_std, torch.float32, dev,
                            seed_of(cid, T_LOGITS))
-    fused = cfg.layout in ("split", "interleaved")
+    # non-gated activations: one fc1 stack [E, I, H] in gate_up_experts
+    fused = cfg.gated and cfg.layout in ("split", "interleaved")
+    two = cfg.gated and not fused
     n_gu = 2 * I if fused else I
     if cfg.w_dtype == "mxfp4":
         out["gate_up_experts"], out["gate_up_scales"] = mxfp4_stack(
             E, n_gu, H, cid, T_GATE_UP, dev)
         out["down_experts"], out["down_scales"] = mxfp4_stack(
             E, H, I, cid, T_DOWN, dev)
-        if not fused:
+        if two:
             out["gate_experts"], out["gate_scales"] = mxfp4_stack(
                 E, I, H, cid, T_UP, dev)
     else:
         wd = _torch_dtype(cfg.w_dtype)
         out["gate_up_experts"] = dense_stack(E, n_gu, H, wd, cid, T_GATE_UP, dev)
         out["down_experts"] = dense_stack(E, H, I, wd, cid, T_DOWN, dev)
-        if not fused:
+        if two:
             out["gate_experts"] = dense_stack(E, I, H, wd, cid, T_UP, dev)
     if cfg.expert_biases:
         out["gate_up_bias"] = normal((E, n_gu), cfg.bias_std, xd, dev,
                                      seed_of(cid, T_GU_BIAS))
         out["down_bias"] = normal((E, H), cfg.bias_std, xd, dev,
                                   seed_of(cid, T_DOWN_BIAS))
-        if not fused:
+        if two:
             out["gate_bias"] = normal((E, I), cfg.bias_std, xd, dev,
                                       seed_of(cid, T_GATE_BIAS))
     if cfg.selection_bias_std is not None:
@@ -213,4 +227,9 @@ def make_inputs(cfg: MoeConfig, device="cpu", T: Optional[int] = None) -> dict:
             seed_of(cid, T_SEL_BIAS))
     if cfg.shared_output:
         out["shared_output"] = normal((T, H), 1.0, xd, dev, seed_of(cid, T_SHARED))
+    if cfg.router:
+        # router Wr [H, E] (the layout of the MoeSpec router index arithmetic)
+        out["router_weight"] = normal((H, E), 1.0 / math.sqrt(H), xd, dev,
+                                      seed_of(cid, T_ROUTER_W))
+        out["router_bias"] = normal((E,), cfg.bias_std, xd, dev, seed_of(cid, T_ROUTER_B))
     return out

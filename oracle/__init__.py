@@ -8,4 +8,4 @@ it with gcc and wraps it with ctypes.  Parity status of each function is listed
 in ``moe_oracle.h``.
 """
 from .oracle import (build, load, params_of, route, permute, forward,  # noqa: F401
-                     mxfp4_value, activation, OrcParams)
+                     router_logits, mxfp4_value, activation, activation1, OrcParams)

@@ -101,7 +101,16 @@ static int check_params(const orc_params *p)
     }
     if (p->w_kind == ORC_MXFP4 && (p->H % 32 != 0 || p->I % 32 != 0))
         return -1;
+    if (p->activation < ORC_SILU_GATED || p->activation > ORC_IDENTITY) return -1;
+    if (p->gelu_mode != ORC_GELU_ERF && p->gelu_mode != ORC_GELU_TANH) return -1;
     return 0;
+}
+
+/* Gated activations read a gate and an up projection; the others one fc1
+ * projection (ONNX MoE: fusion_size 2 for fused swiglu, 1 otherwise). */
+static int is_gated(const orc_params *p)
+{
+    return p->activation == ORC_SILU_GATED || p->activation == ORC_SWIGLU_CLAMPED;
 }
 
 /* Route one token.
@@ -266,6 +275,61 @@ double orc_activation(const orc_params *p, double g, double u)
     return g * (1.0 / (1.0 + exp(-p->alpha * g))) * (u + p->beta);
 }
 
+/* Activation of a non-gated expert (ONNX MoE `activation_type` relu, gelu,
+ * silu, identity on the fc1 output; clika MoE option `gelu_mode`):
+ *   relu(v) = max(v, 0);  silu(v) = v * sigmoid(v);  identity(v) = v;
+ *   gelu(v) = v * Phi(v) with Phi the standard normal CDF,
+ *             Phi(v) = (1 + erf(v / sqrt 2)) / 2            (gelu_mode erf),
+ *   or its tanh approximation
+ *             (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))) / 2  (gelu_mode tanh).
+ * The pages name gelu_mode without printing either form; both are the
+ * published GELU definitions. */
+double orc_activation1(const orc_params *p, double v)
+{
+    switch (p->activation) {
+    case ORC_RELU: return v > 0.0 ? v : 0.0;
+    case ORC_SILU: return v * (1.0 / (1.0 + exp(-v)));
+    case ORC_IDENTITY: return v;
+    case ORC_GELU:
+        if (p->gelu_mode == ORC_GELU_TANH) {
+            const double c = sqrt(2.0 / acos(-1.0));
+            return 0.5 * v * (1.0 + tanh(c * (v + 0.044715 * v * v * v)));
+        }
+        return 0.5 * v * (1.0 + erf(v / sqrt(2.0)));
+    default: return NAN;
+    }
+}
+
+/* Router logits (MoeSpec `wr`, `router_bias`: wr[(t-1)E + e] indexes a
+ * [d, E] matrix; the bias is added to each logit before scoring):
+ * l[e] = sum_c x[c] * Wr[c, e] + Br[e], in fp64. */
+static void router_logits_token(const orc_params *p, const orc_inputs *in, const double *xv,
+                                double *l)
+{
+    const int64_t H = p->H, E = p->E;
+    for (int64_t e = 0; e < E; ++e) {
+        double v = 0.0;
+        for (int64_t c = 0; c < H; ++c)
+            v += xv[c] * elem(p->x_kind, in->router_w, c * E + e);
+        if (in->router_b) v += elem(p->x_kind, in->router_b, e);
+        l[e] = v;
+    }
+}
+
+int orc_router_logits(const orc_params *p, const orc_inputs *in, double *logits)
+{
+    if (check_params(p) || !in->router_w) return -1;
+    const int64_t H = p->H, E = p->E;
+    double *xv = (double *)malloc(sizeof(double) * H);
+    for (int64_t t = 0; t < p->T; ++t) {
+        for (int64_t c = 0; c < H; ++c)
+            xv[c] = elem(p->x_kind, in->x, t * H + c);
+        router_logits_token(p, in, xv, logits + t * E);
+    }
+    free(xv);
+    return 0;
+}
+
 typedef struct {
     const orc_params *p;
     const orc_inputs *in;
@@ -282,24 +346,42 @@ typedef struct {
  * router weights (clika MoE: "the outputs combine under the router weights";
  * MoeSpec: `out` is the tensor the weighted accumulation writes), and fold the
  * optional shared-expert output into the same sum (QMoEWoQ::forward). */
+/*
+ * With a bound router the token's logits are x . Wr + Br, rounded to f32 (the
+ * precision in which they are stored and the discrete choices are taken).
+ * Weigh-inputs routing (MoeSpec `weigh_inputs`, Llama 4; clika MoE option
+ * apply_router_weight_on_input): expert j reads w_j * x and its output joins
+ * the sum with weight one.
+ */
 static void token_forward(const orc_params *p, const orc_inputs *in, int64_t t,
                           double *out, int32_t *ids, double *w, double *hdump,
-                          double *ydump, double *xv, double *hv, double *yv,
-                          double *sc, double *ky)
+                          double *ydump, double *x0, double *hv, double *yv,
+                          double *sc, double *ky, double *xv, float *lf, double *ld)
 {
     const int64_t H = p->H, I = p->I, E = p->E, K = p->K;
-    const int fused = p->layout != ORC_UNFUSED;
+    const int gated = is_gated(p);
+    const int fused = gated && p->layout != ORC_UNFUSED;
     const int64_t gu_rows = fused ? 2 * I : I;
 
-    route_token(p, in->logits + t * E, in->sel_bias, ids, w, sc, ky);
-
     for (int64_t c = 0; c < H; ++c)
-        xv[c] = elem(p->x_kind, in->x, t * H + c);
+        x0[c] = elem(p->x_kind, in->x, t * H + c);
+    const float *lt = in->logits ? in->logits + t * E : NULL;
+    if (in->router_w) {
+        router_logits_token(p, in, x0, ld);
+        for (int64_t e = 0; e < E; ++e) lf[e] = (float)ld[e];
+        lt = lf;
+    }
+    route_token(p, lt, in->sel_bias, ids, w, sc, ky);
+
     for (int64_t c = 0; c < H; ++c)
         out[c] = 0.0;
 
     for (int64_t j = 0; j < K; ++j) {
         const int64_t e = ids[j];
+        const double xs = p->weigh_inputs ? w[j] : 1.0;     /* input scale  */
+        const double ws = p->weigh_inputs ? 1.0 : w[j];     /* output weight */
+        for (int64_t c = 0; c < H; ++c)
+            xv[c] = xs * x0[c];
         /* expert e's slabs */
         const char *gu = (const char *)in->w_gu + e * mat_elems_bytes(p->w_kind, gu_rows, H);
         const uint8_t *gus = in->w_gu_scales ? in->w_gu_scales + e * gu_rows * (H / 32) : NULL;
@@ -308,7 +390,13 @@ static void token_forward(const orc_params *p, const orc_inputs *in, int64_t t,
         const char *dn = (const char *)in->w_down + e * mat_elems_bytes(p->w_kind, H, I);
         const uint8_t *dns = in->w_down_scales ? in->w_down_scales + e * H * (I / 32) : NULL;
 
-        for (int64_t o = 0; o < I; ++o) {
+        for (int64_t o = 0; o < I && !gated; ++o) {
+            /* non-gated: one fc1 row per feature ([E, I, H], bias [E, I]) */
+            double v = dot_row(p->w_kind, gu, gus, o, H, xv);
+            if (in->b_gu) v += elem(p->x_kind, in->b_gu, e * I + o);
+            hv[o] = orc_activation1(p, v);
+        }
+        for (int64_t o = 0; o < I && gated; ++o) {
             /* gate/up rows per ONNX MoE `swiglu_fusion`: 2 = fused, not
              * interleaved (gate rows [0,I), up rows [I,2I)); 1 = fused,
              * interleaved (gate 2o, up 2o+1); 0 = not fused (gate stack and
@@ -343,7 +431,7 @@ static void token_forward(const orc_params *p, const orc_inputs *in, int64_t t,
             yv[c] = v;
         }
         for (int64_t c = 0; c < H; ++c)
-            out[c] += w[j] * yv[c];
+            out[c] += ws * yv[c];
         if (hdump) memcpy(hdump + j * I, hv, sizeof(double) * I);
         if (ydump) memcpy(ydump + j * H, yv, sizeof(double) * H);
     }
@@ -357,18 +445,21 @@ static void *worker(void *arg)
     job_t *jb = (job_t *)arg;
     const orc_params *p = jb->p;
     const int64_t H = p->H, I = p->I, K = p->K, E = p->E;
+    double *x0 = (double *)malloc(sizeof(double) * H);
     double *xv = (double *)malloc(sizeof(double) * H);
     double *hv = (double *)malloc(sizeof(double) * I);
     double *yv = (double *)malloc(sizeof(double) * H);
     double *sc = (double *)malloc(sizeof(double) * E);
     double *ky = (double *)malloc(sizeof(double) * E);
+    double *ld = (double *)malloc(sizeof(double) * E);
+    float *lf = (float *)malloc(sizeof(float) * E);
     for (int64_t i = jb->tid; i < jb->n; i += jb->nthreads) {
         int64_t t = jb->tokens ? jb->tokens[i] : i;
         token_forward(p, jb->in, t, jb->out + i * H, jb->ids + i * K,
                       jb->weights + i * K, jb->h ? jb->h + i * K * I : NULL,
-                      jb->y ? jb->y + i * K * H : NULL, xv, hv, yv, sc, ky);
+                      jb->y ? jb->y + i * K * H : NULL, x0, hv, yv, sc, ky, xv, lf, ld);
     }
-    free(xv); free(hv); free(yv); free(sc); free(ky);
+    free(x0); free(xv); free(hv); free(yv); free(sc); free(ky); free(ld); free(lf);
     return NULL;
 }
 
@@ -377,10 +468,12 @@ int orc_forward(const orc_params *p, const orc_inputs *in, int64_t n,
                 int32_t *ids, double *weights, double *h, double *y)
 {
     if (check_params(p)) return -1;
-    if (p->layout == ORC_UNFUSED && !in->w_gate) return -1;
+    const int two_stacks = is_gated(p) && p->layout == ORC_UNFUSED;
+    if (two_stacks && !in->w_gate) return -1;
     if (p->w_kind == ORC_MXFP4 && (!in->w_gu_scales || !in->w_down_scales ||
-                                   (p->layout == ORC_UNFUSED && !in->w_gate_scales)))
+                                   (two_stacks && !in->w_gate_scales)))
         return -1;
+    if (!in->logits && !in->router_w) return -1;
     if (tokens)
         for (int64_t i = 0; i < n; ++i)
             if (tokens[i] < 0 || tokens[i] >= p->T) return -1;

@@ -15,6 +15,12 @@
  *       the pages name the three parameters but print no formula.
  *   MXFP4 decode                                                  -- pinned to
  *       the OCP MX v1.0 e2m1 / e8m0 tables (public spec, not the pages).
+ *   non-gated activations relu / gelu / silu / identity           -- pinned
+ *       (closed forms, tabulated normal CDF, linear-FFN reduction); the tanh
+ *       form of gelu is pinned only by its identities and its distance to
+ *       the erf form (the pages name gelu_mode but print neither form).
+ *   weigh-inputs routing                                          -- pinned
+ *   router logits x . Wr + Br                                     -- pinned
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -28,7 +34,9 @@ extern "C" {
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2 };                 /* storage kinds   */
 enum { ORC_UNFUSED = 0, ORC_INTERLEAVED = 1, ORC_SPLIT = 2 };       /* swiglu_fusion   */
 enum { ORC_SOFTMAX = 0, ORC_SIGMOID = 1 };                          /* scoring         */
-enum { ORC_SILU_GATED = 0, ORC_SWIGLU_CLAMPED = 1 };                /* gated activation*/
+enum { ORC_SILU_GATED = 0, ORC_SWIGLU_CLAMPED = 1,                 /* gated (fc1||fc3) */
+       ORC_RELU = 2, ORC_GELU = 3, ORC_SILU = 4, ORC_IDENTITY = 5 }; /* one fc1 stack   */
+enum { ORC_GELU_ERF = 0, ORC_GELU_TANH = 1 };                       /* gelu_mode       */
 
 typedef struct {
     int64_t T, H, I, E, K;
@@ -39,9 +47,12 @@ typedef struct {
     int32_t renormalize;
     int32_t n_group;         /* 0 = no group limit                           */
     int32_t topk_group;
-    int32_t activation;      /* ORC_SILU_GATED / ORC_SWIGLU_CLAMPED           */
+    int32_t activation;      /* ORC_SILU_GATED ... ORC_IDENTITY               */
     double routed_scaling_factor;
     double alpha, beta, limit;
+    int32_t gelu_mode;       /* ORC_GELU_ERF / ORC_GELU_TANH                  */
+    int32_t weigh_inputs;    /* kept weight scales the expert's input; the
+                                outputs then sum unweighted                   */
 } orc_params;
 
 typedef struct {
@@ -58,6 +69,9 @@ typedef struct {
     const void *b_down;         /* [E,H]; nullable                               */
     const float *sel_bias;      /* [E] selection bias; nullable                  */
     const void *shared_output;  /* [T,H] x_kind; nullable                        */
+    const void *router_w;       /* [H,E] x_kind; when set, logits = x.Wr (+Br)
+                                   and `logits` is not read                      */
+    const void *router_b;       /* [E] x_kind; nullable                          */
 } orc_inputs;
 
 /* Routing for every token: ids [T,K] in rank order, weights [T,K] (fp64),
@@ -80,7 +94,11 @@ int orc_forward(const orc_params *p, const orc_inputs *in, int64_t n,
                 const int64_t *tokens, int n_threads, double *out,
                 int32_t *ids, double *weights, double *h, double *y);
 
+/* Router logits of every token, fp64 [T,E]: x . Wr + Br (needs router_w). */
+int orc_router_logits(const orc_params *p, const orc_inputs *in, double *logits);
+
 /* Helpers exposed for the pins. */
+double orc_activation1(const orc_params *p, double v);
 double orc_mxfp4_value(uint8_t code4, uint8_t scale_byte);
 double orc_activation(const orc_params *p, double g, double u);
 double orc_bf16_to_double(uint16_t bits);

@@ -19,7 +19,9 @@ _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 ORC_F32, ORC_BF16, ORC_MXFP4 = 0, 1, 2
 LAYOUTS = {"unfused": 0, "interleaved": 1, "split": 2}
 SCORING = {"softmax": 0, "sigmoid": 1}
-ACTS = {"silu": 0, "swiglu_clamped": 1}
+ACTS = {"silu": 0, "swiglu_clamped": 1, "relu": 2, "gelu": 3, "silu_plain": 4,
+        "identity": 5}
+GELU_MODES = {"erf": 0, "tanh": 1}
 KINDS = {"f32": ORC_F32, "bf16": ORC_BF16, "mxfp4": ORC_MXFP4}
 
 
@@ -31,14 +33,15 @@ class OrcParams(C.Structure):
                 ("renormalize", C.c_int32), ("n_group", C.c_int32),
                 ("topk_group", C.c_int32), ("activation", C.c_int32),
                 ("routed_scaling_factor", C.c_double),
-                ("alpha", C.c_double), ("beta", C.c_double), ("limit", C.c_double)]
+                ("alpha", C.c_double), ("beta", C.c_double), ("limit", C.c_double),
+                ("gelu_mode", C.c_int32), ("weigh_inputs", C.c_int32)]
 
 
 class OrcInputs(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "x", "logits", "w_gu", "w_gu_scales", "w_gate", "w_gate_scales",
         "w_down", "w_down_scales", "b_gu", "b_gate", "b_down", "sel_bias",
-        "shared_output")]
+        "shared_output", "router_w", "router_b")]
 
 
 def build(force: bool = False) -> str:
@@ -73,6 +76,11 @@ def load():
         lib.orc_mxfp4_value.restype = C.c_double
         lib.orc_activation.argtypes = [C.POINTER(OrcParams), C.c_double, C.c_double]
         lib.orc_activation.restype = C.c_double
+        lib.orc_activation1.argtypes = [C.POINTER(OrcParams), C.c_double]
+        lib.orc_activation1.restype = C.c_double
+        lib.orc_router_logits.argtypes = [C.POINTER(OrcParams), C.POINTER(OrcInputs),
+                                          C.c_void_p]
+        lib.orc_router_logits.restype = C.c_int
         lib.orc_bf16_to_double.argtypes = [C.c_uint16]
         lib.orc_bf16_to_double.restype = C.c_double
         _lib = lib
@@ -87,7 +95,8 @@ def params_of(cfg, T: Optional[int] = None, **over) -> OrcParams:
              renormalize=int(cfg.renormalize), n_group=cfg.n_group,
              topk_group=cfg.topk_group, activation=ACTS[cfg.activation],
              routed_scaling_factor=cfg.routed_scaling_factor,
-             alpha=cfg.swiglu_alpha, beta=cfg.swiglu_beta, limit=cfg.swiglu_limit)
+             alpha=cfg.swiglu_alpha, beta=cfg.swiglu_beta, limit=cfg.swiglu_limit,
+             gelu_mode=GELU_MODES[cfg.gelu_mode], weigh_inputs=int(cfg.weigh_inputs))
     d.update(over)
     return OrcParams(**d)
 
@@ -153,27 +162,44 @@ def permute(p: OrcParams, ids):
                 slot_row=slot_row)
 
 
-def forward(p: OrcParams, inp: dict, tokens=None, threads: Optional[int] = None,
-            stages: bool = False):
-    """Forward of the layer on `tokens` (None: all).  `inp` uses the slot
-    names of ``synth.make_inputs``.  Returns dict(out [n,H] f64, ids, weights,
-    and with stages=True h [n,K,I], y [n,K,H])."""
-    lib = load()
-    keep = {}
-
+def _inputs(inp: dict, keep: dict, use_router: bool) -> OrcInputs:
     def arr(name, dtype=None):
         a = _np(inp.get(name), dtype)
         keep[name] = a
         return _ptr(a)
 
-    ins = OrcInputs(
-        x=arr("x"), logits=arr("logits", np.float32),
+    return OrcInputs(
+        x=arr("x"), logits=None if use_router else arr("logits", np.float32),
         w_gu=arr("gate_up_experts"), w_gu_scales=arr("gate_up_scales", np.uint8),
         w_gate=arr("gate_experts"), w_gate_scales=arr("gate_scales", np.uint8),
         w_down=arr("down_experts"), w_down_scales=arr("down_scales", np.uint8),
         b_gu=arr("gate_up_bias"), b_gate=arr("gate_bias"), b_down=arr("down_bias"),
         sel_bias=arr("e_score_correction_bias", np.float32),
-        shared_output=arr("shared_output"))
+        shared_output=arr("shared_output"),
+        router_w=arr("router_weight") if use_router else None,
+        router_b=arr("router_bias") if use_router else None)
+
+
+def router_logits(p: OrcParams, inp: dict) -> np.ndarray:
+    """fp64 router logits [T,E] = x . Wr + Br from inp's router_weight [H,E]
+    and optional router_bias [E]."""
+    keep = {}
+    ins = _inputs(inp, keep, True)
+    out = np.zeros((p.T, p.E), np.float64)
+    if load().orc_router_logits(C.byref(p), C.byref(ins), _ptr(out)) != 0:
+        raise ValueError("oracle rejected the router inputs")
+    return out
+
+
+def forward(p: OrcParams, inp: dict, tokens=None, threads: Optional[int] = None,
+            stages: bool = False, use_router: bool = False):
+    """Forward of the layer on `tokens` (None: all).  `inp` uses the slot
+    names of ``synth.make_inputs``; with use_router the logits come from its
+    router_weight / router_bias instead of its logits.  Returns dict(out [n,H]
+    f64, ids, weights, and with stages=True h [n,K,I], y [n,K,H])."""
+    lib = load()
+    keep = {}
+    ins = _inputs(inp, keep, use_router)
     x = keep["x"]
     assert x.shape == (p.T, p.H), (x.shape, p.T, p.H)
     if tokens is None:
@@ -204,3 +230,7 @@ def mxfp4_value(code4: int, scale_byte: int) -> float:
 
 def activation(p: OrcParams, g: float, u: float) -> float:
     return load().orc_activation(C.byref(p), g, u)
+
+
+def activation1(p: OrcParams, v: float) -> float:
+    return load().orc_activation1(C.byref(p), v)

@@ -451,3 +451,182 @@ def test_invalid_options_are_rejected(orc):
         orc.route(_params(orc, 2, 8, 2, n_group=3, topk_group=1), np.zeros((2, 8), np.float32))
     with pytest.raises(ValueError):   # K > eligible experts
         orc.route(_params(orc, 2, 8, 5, n_group=4, topk_group=2), np.zeros((2, 8), np.float32))
+
+
+# --------------------------------------------------- non-gated activation pins
+
+def _act_params(orc, act, gelu_mode="erf"):
+    cfg = synth.MoeConfig(name="a1", cid=120, T=1, H=8, I=4, E=2, K=1, x_dtype="f32",
+                          w_dtype="f32", activation=act, gelu_mode=gelu_mode)
+    return orc.params_of(cfg)
+
+
+def test_relu_silu_identity_closed_forms(orc):
+    """ONNX MoE activation_type relu / silu / identity on the fc1 output."""
+    p = _act_params(orc, "relu")
+    assert orc.activation1(p, 2.5) == 2.5 and orc.activation1(p, -1.0) == 0.0
+    assert orc.activation1(p, 0.0) == 0.0
+    p = _act_params(orc, "identity")
+    for v in (-3.25, 0.0, 7.5):
+        assert orc.activation1(p, v) == v
+    p = _act_params(orc, "silu_plain")
+    assert orc.activation1(p, 0.0) == 0.0
+    # silu(1) = 1 / (1 + e^-1) = e / (1 + e)
+    assert abs(orc.activation1(p, 1.0) - math.e / (1.0 + math.e)) < 1e-16
+    # silu(v) -> v for large v, -> 0 for very negative v
+    assert abs(orc.activation1(p, 40.0) - 40.0) < 1e-12
+    assert abs(orc.activation1(p, -40.0)) < 1e-15
+
+
+# Standard normal CDF at 1, 2, 0.5 (tabulated values of Phi, e.g. any table of
+# the normal distribution): gelu(v) = v * Phi(v) in its exact (erf) form.
+PHI = {1.0: 0.8413447460685429, 2.0: 0.9772498680518208, 0.5: 0.6914624612740131}
+
+
+def test_gelu_erf_tabulated(orc):
+    p = _act_params(orc, "gelu", "erf")
+    for v, phi in PHI.items():
+        assert abs(orc.activation1(p, v) - v * phi) < 1e-15 * max(1.0, v)
+        # Phi(-v) = 1 - Phi(v)
+        assert abs(orc.activation1(p, -v) - (-v) * (1.0 - phi)) < 1e-15 * max(1.0, v)
+    assert orc.activation1(p, 0.0) == 0.0
+
+
+def test_gelu_tanh_identities_and_distance(orc):
+    """The tanh form keeps gelu(v) - gelu(-v) = v and stays within 1e-3 of the
+    erf form (it is an approximation of it), but is not equal to it."""
+    pt = _act_params(orc, "gelu", "tanh")
+    pe = _act_params(orc, "gelu", "erf")
+    worst = 0.0
+    for v in np.linspace(-6.0, 6.0, 241):
+        v = float(v)
+        a, b = orc.activation1(pt, v), orc.activation1(pt, -v)
+        assert abs((a - b) - v) < 1e-14 * max(1.0, abs(v))
+        worst = max(worst, abs(a - orc.activation1(pe, v)))
+    assert 1e-5 < worst < 1e-3
+
+
+def _single_ffn_np(W1, Wd, x, act, b1=None, bd=None):
+    """Textbook non-gated FFN with numpy float64 matmuls."""
+    v = W1 @ x + (0 if b1 is None else b1)
+    h = {"relu": np.maximum(v, 0.0), "identity": v}[act]
+    return Wd @ h + (0 if bd is None else bd)
+
+
+@pytest.mark.parametrize("act", ["relu", "identity"])
+def test_nongated_single_expert_is_the_textbook_ffn(orc, act):
+    """E=1, K=1, renormalised, one fc1 stack [E, I, H] with bias (ONNX MoE
+    fusion_size 1): the layer is W_d act(W_1 x + b_1) + b_d."""
+    cfg = synth.MoeConfig(name="ng", cid=121, T=7, H=24, I=16, E=1, K=1, x_dtype="f32",
+                          w_dtype="f32", activation=act, expert_biases=True,
+                          bias_std=0.5)
+    inp = synth.make_inputs(cfg)
+    assert inp["gate_up_experts"].shape == (1, 16, 24) and "gate_experts" not in inp
+    r = orc.forward(orc.params_of(cfg), inp)
+    W1, Wd, X = _f64(inp["gate_up_experts"][0]), _f64(inp["down_experts"][0]), _f64(inp["x"])
+    b1, bd = _f64(inp["gate_up_bias"][0]), _f64(inp["down_bias"][0])
+    want = np.stack([_single_ffn_np(W1, Wd, X[t], act, b1, bd) for t in range(cfg.T)])
+    np.testing.assert_allclose(r["out"], want, rtol=1e-12, atol=1e-13)
+
+
+def test_identity_layer_is_the_weighted_linear_map(orc):
+    """Identity activation, no biases: each expert is the linear map W_d W_1,
+    so out = sum_j w_j W_d[e_j] W_1[e_j] x for any routing."""
+    cfg = synth.MoeConfig(name="lin", cid=122, T=11, H=16, I=12, E=5, K=3, x_dtype="f32",
+                          w_dtype="f32", activation="identity", renormalize=False)
+    inp = synth.make_inputs(cfg)
+    r = orc.forward(orc.params_of(cfg), inp)
+    W1, Wd, X = _f64(inp["gate_up_experts"]), _f64(inp["down_experts"]), _f64(inp["x"])
+    want = np.zeros((cfg.T, cfg.H))
+    for t in range(cfg.T):
+        for j in range(cfg.K):
+            e = r["ids"][t, j]
+            want[t] += r["weights"][t, j] * (Wd[e] @ (W1[e] @ X[t]))
+    np.testing.assert_allclose(r["out"], want, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------- weigh-inputs pins
+
+def test_weigh_inputs_with_unit_weights_changes_nothing(orc):
+    """K = 1 renormalised: the one kept weight is 1, so scaling the input or
+    the output by it gives the same layer (MoeSpec `weigh_inputs`)."""
+    cfg = synth.MoeConfig(name="wi1", cid=123, T=13, H=32, I=16, E=4, K=1, x_dtype="f32",
+                          w_dtype="f32", layout="split", expert_biases=True)
+    inp = synth.make_inputs(cfg)
+    a = orc.forward(orc.params_of(cfg), inp)
+    b = orc.forward(orc.params_of(cfg.replace(weigh_inputs=True)), inp)
+    assert (a["ids"] == b["ids"]).all()
+    np.testing.assert_allclose(b["out"], a["out"], rtol=1e-14, atol=1e-15)
+
+
+def test_weigh_inputs_on_a_linear_layer_equals_weigh_outputs(orc):
+    """Identity activation and no biases make every expert linear, so
+    FFN(w x) = w FFN(x): both routings give the same output; with biases
+    (not homogeneous) they differ."""
+    cfg = synth.MoeConfig(name="wi2", cid=124, T=10, H=16, I=8, E=6, K=3, x_dtype="f32",
+                          w_dtype="f32", activation="identity", renormalize=False)
+    inp = synth.make_inputs(cfg)
+    a = orc.forward(orc.params_of(cfg), inp)
+    b = orc.forward(orc.params_of(cfg.replace(weigh_inputs=True)), inp)
+    np.testing.assert_allclose(b["out"], a["out"], rtol=1e-12, atol=1e-14)
+    cfgb = cfg.replace(expert_biases=True, bias_std=1.0)
+    inpb = synth.make_inputs(cfgb)
+    a = orc.forward(orc.params_of(cfgb), inpb)
+    b = orc.forward(orc.params_of(cfgb.replace(weigh_inputs=True)), inpb)
+    assert np.abs(b["out"] - a["out"]).max() > 1e-3
+
+
+def test_weigh_inputs_single_expert_is_the_ffn_of_the_scaled_input(orc):
+    """E=1, K=1, sigmoid scoring without renormalisation: the weight is
+    sigma(l), and the layer is the textbook FFN evaluated at sigma(l) x."""
+    cfg = synth.MoeConfig(name="wi3", cid=125, T=9, H=24, I=16, E=1, K=1, x_dtype="f32",
+                          w_dtype="f32", layout="split", scoring="sigmoid",
+                          renormalize=False, weigh_inputs=True)
+    inp = synth.make_inputs(cfg)
+    r = orc.forward(orc.params_of(cfg), inp)
+    W, Wd, X = _f64(inp["gate_up_experts"][0]), _f64(inp["down_experts"][0]), _f64(inp["x"])
+    s = _sigmoid(inp["logits"].numpy().astype(np.float64)[:, 0])
+    want = np.stack([_ffn_np(W[:16], W[16:], Wd, s[t] * X[t]) for t in range(cfg.T)])
+    np.testing.assert_allclose(r["out"], want, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------ router pins
+
+def test_router_logits_are_x_times_Wr_plus_Br(orc):
+    """MoeSpec router: logits = x . Wr + Br with Wr indexed [d, E]; checked
+    against numpy's float64 matmul."""
+    cfg = synth.MoeConfig(name="rt", cid=126, T=17, H=40, I=8, E=12, K=2, x_dtype="bf16",
+                          w_dtype="bf16", router=True, bias_std=0.3)
+    inp = synth.make_inputs(cfg)
+    lg = orc.router_logits(orc.params_of(cfg), inp)
+    want = _f64(inp["x"]) @ _f64(inp["router_weight"]) + _f64(inp["router_bias"])
+    np.testing.assert_allclose(lg, want, rtol=1e-13, atol=1e-14)
+
+
+def test_router_with_identity_weights_routes_on_x(orc):
+    """H = E, Wr = identity, no bias: the router logits are x itself, so the
+    layer equals the one fed logits = x."""
+    cfg = synth.MoeConfig(name="rt2", cid=127, T=14, H=16, I=8, E=16, K=3, x_dtype="f32",
+                          w_dtype="f32", router=True, layout="interleaved")
+    inp = synth.make_inputs(cfg)
+    inp["router_weight"] = torch.eye(16, dtype=torch.float32)
+    del inp["router_bias"]
+    a = orc.forward(orc.params_of(cfg), inp, use_router=True)
+    inp2 = dict(inp)
+    inp2["logits"] = inp["x"].clone()
+    b = orc.forward(orc.params_of(cfg), inp2)
+    assert (a["ids"] == b["ids"]).all()
+    assert (a["out"] == b["out"]).all()
+
+
+def test_router_bias_alone_sets_every_tokens_logits(orc):
+    """Wr = 0: every token's logits are Br, so every token keeps the same
+    experts, the K largest of Br."""
+    cfg = synth.MoeConfig(name="rt3", cid=128, T=6, H=8, I=8, E=10, K=3, x_dtype="f32",
+                          w_dtype="f32", router=True, bias_std=1.0)
+    inp = synth.make_inputs(cfg)
+    inp["router_weight"] = torch.zeros_like(inp["router_weight"])
+    r = orc.forward(orc.params_of(cfg), inp, use_router=True)
+    br = inp["router_bias"].numpy()
+    want = np.argsort(-br, kind="stable")[:3]
+    assert (r["ids"] == want[None, :]).all()
