@@ -60,18 +60,32 @@ typedef enum moe_dtype {
 /* MoeSpec `score`: softmax over every logit, or each logit's own sigmoid. */
 typedef enum moe_scoring { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 } moe_scoring;
 
-/* Gated activation: SiLU-gated h = silu(g)*u, or the clamped SwiGLU
- * h = g'*sigmoid(alpha*g')*(u'+beta), g' = min(g,L), u' = clamp(u,-L,L),
- * L = swiglu_limit (L <= 0: no clamp) -- ONNX MoE activation_alpha/beta and
- * swiglu_limit; clika MoE options swiglu_alpha/beta/limit. */
+/* Expert activation (ONNX MoE `activation_type`; clika MoE option
+ * `activation`).  Gated (two projections, gate and up):
+ *   SILU_GATED      h = silu(g)*u
+ *   SWIGLU_CLAMPED  h = g'*sigmoid(alpha*g')*(u'+beta), g' = min(g,L),
+ *                   u' = clamp(u,-L,L), L = swiglu_limit (L <= 0: no clamp)
+ *                   -- ONNX MoE activation_alpha/beta and swiglu_limit; clika
+ *                   MoE options swiglu_alpha/beta/limit.
+ * Non-gated (one fc1 projection v, ONNX MoE fusion_size 1):
+ *   RELU max(v,0); GELU v*Phi(v) (gelu_mode: erf form or tanh form);
+ *   SILU v*sigmoid(v); IDENTITY v. */
 typedef enum moe_activation {
     MOE_ACT_SILU_GATED = 0,
-    MOE_ACT_SWIGLU_CLAMPED = 1
+    MOE_ACT_SWIGLU_CLAMPED = 1,
+    MOE_ACT_RELU = 2,
+    MOE_ACT_GELU = 3,
+    MOE_ACT_SILU = 4,
+    MOE_ACT_IDENTITY = 5
 } moe_activation;
+
+/* clika MoE option `gelu_mode`: Phi(v) = (1+erf(v/sqrt 2))/2, or the tanh
+ * approximation (1+tanh(sqrt(2/pi)(v+0.044715 v^3)))/2. */
+typedef enum moe_gelu_mode { MOE_GELU_ERF = 0, MOE_GELU_TANH = 1 } moe_gelu_mode;
 
 /* ONNX MoE `swiglu_fusion`: 0 not fused (separate gate and up stacks),
  * 1 fused interleaved (row 2i gate, 2i+1 up), 2 fused not interleaved
- * (rows [0,I) gate, [I,2I) up). */
+ * (rows [0,I) gate, [I,2I) up).  Non-gated activations ignore it. */
 typedef enum moe_swiglu_fusion {
     MOE_FUSION_NONE = 0,
     MOE_FUSION_INTERLEAVED = 1,
@@ -100,6 +114,12 @@ typedef struct moe_options {
                                      tiles, 2 small-M (decode, 32-row) tiles, 3
                                      mid (128-row) tiles; f32 layers ignore it.
                                      Default 0                                     */
+    int32_t gelu_mode;            /* moe_gelu_mode; default ERF                      */
+    int32_t weigh_inputs;         /* MoeSpec `weigh_inputs` (clika MoE
+                                     apply_router_weight_on_input, Llama 4): a kept
+                                     expert's weight scales the input it reads and
+                                     its output joins the sum unweighted.  0 or 1;
+                                     default 0                                      */
 } moe_options;
 
 /* A device tensor view.  ndim == 0 (or data == NULL) marks an absent tensor.
@@ -114,17 +134,25 @@ typedef struct moe_tensor {
 } moe_tensor;
 
 /* Weight slots, named as clika MoE.set_weights / QMoEWoQ::set_weights.
- *  gate_up_experts : fused [E, 2I, H] (layout per swiglu_fusion);
- *                    not fused: the UP rows [E, I, H]
- *  gate_experts    : not fused only: the GATE rows [E, I, H]
+ *  gate_up_experts : gated, fused [E, 2I, H] (layout per swiglu_fusion);
+ *                    gated, not fused: the UP rows [E, I, H];
+ *                    non-gated activation: the fc1 rows [E, I, H]
+ *  gate_experts    : gated, not fused only: the GATE rows [E, I, H]
  *  down_experts    : [E, H, I]
- *  gate_up_bias    : fused [E, 2I]; not fused: up bias [E, I]   (x dtype)
- *  gate_bias       : not fused only: gate bias [E, I]           (x dtype)
- *  down_bias       : [E, H]                                     (x dtype)
+ *  gate_up_bias    : fused [E, 2I]; otherwise up / fc1 bias [E, I] (x dtype)
+ *  gate_bias       : gated, not fused only: gate bias [E, I]      (x dtype)
+ *  down_bias       : [E, H]                                       (x dtype)
  *  e_score_correction_bias : [E] f32 selection bias; binds even when no bias
  *                    was declared (clika MoE.set_weights).  It is added to the
  *                    score for SELECTION only; weights use the score alone
- *                    (MoeSpec `selection_bias`). */
+ *                    (MoeSpec `selection_bias`).
+ *  router_weight   : optional router Wr [H, E] (x dtype; MoeSpec `wr`, whose
+ *                    index arithmetic makes it [d, E]); when bound, a forward
+ *                    without router_logits computes logits = x . Wr + Br.
+ *                    Binds whatever was declared, like the selection bias.
+ *  router_bias     : optional router bias Br [E] (x dtype; MoeSpec
+ *                    `router_bias`, added to each logit before scoring); needs
+ *                    router_weight. */
 typedef struct moe_weights {
     moe_tensor gate_up_experts;
     moe_tensor down_experts;
@@ -133,6 +161,8 @@ typedef struct moe_weights {
     moe_tensor down_bias;
     moe_tensor gate_bias;
     moe_tensor e_score_correction_bias;
+    moe_tensor router_weight;
+    moe_tensor router_bias;
 } moe_weights;
 
 /* Optional copies of the routing state of a forward (all DEVICE pointers,
@@ -159,8 +189,10 @@ moe_status moe_options_default(moe_options *opts);
  * MXFP4), which bias slots exist, and the options (NULL = defaults).
  * Validation: E <= 1024; H <= 2^20; I <= 131072; with a group limit,
  * E % n_group == 0 and top_k <= topk_group * E / n_group; MXFP4 needs H and I
- * multiples of 32; dense weights need H and I multiples of 8.  The handle owns no device
- * memory.  Errors: INVALID_ARGUMENT. */
+ * multiples of 32; dense weights need H and I multiples of 8.  The handle
+ * allocates device memory only at prepare: the packed copy of MXFP4 weights
+ * and the transposed router, both freed by moe_destroy.
+ * Errors: INVALID_ARGUMENT. */
 moe_status moe_create(int64_t num_experts, int64_t hidden_size,
                       int64_t intermediate_size, int64_t top_k,
                       moe_dtype weight_dtype, int has_gate_up_bias,
@@ -175,8 +207,11 @@ moe_status moe_create(int64_t num_experts, int64_t hidden_size,
  * without its declared slot). */
 moe_status moe_set_weights(moe_layer *layer, const moe_weights *w);
 
-/* Optional warm-up (QMoEWoQ::initialize): checks that every declared slot is
- * bound.  Idempotent.  Errors: UNBOUND. */
+/* Optional warm-up (QMoEWoQ::initialize, "pack once"): checks that every
+ * declared slot is bound, scans the down weights for exact fp16 conversion,
+ * packs MXFP4 stacks into the layout the GEMMs stream and transposes a bound
+ * router.  Runs once per binding (a forward runs it if needed) and
+ * synchronises `stream`.  Errors: UNBOUND, HIP. */
 moe_status moe_prepare(moe_layer *layer, void *stream);
 
 /* Device workspace bytes a forward (or moe_route) on T tokens needs.  The
@@ -186,6 +221,8 @@ moe_status moe_workspace_size(const moe_layer *layer, int64_t T, size_t *bytes);
 
 /* One MoE step (QMoEWoQ::forward): x [T, H] (or [B, S, H]) and the
  * caller-computed router_logits [T, E] f32 -> out with x's shape and dtype.
+ * router_logits may be NULL (or ndim 0) when router_weight is bound: the
+ * logits are then x . Wr + Br, computed on the GPU (f32 accumulation).
  * x dtype: F32 for F32 weights, BF16 for BF16 or MXFP4 weights.  Optional
  * shared_output (the shared-expert branch, EXACTLY x's shape and dtype) is
  * added inside the combine.  `routing` (nullable) receives copies of the
@@ -217,6 +254,13 @@ moe_status moe_forward_timed(const moe_layer *layer, const moe_tensor *x,
 moe_status moe_route(const moe_layer *layer, const moe_tensor *router_logits,
                      moe_routing_out *routing, void *workspace,
                      size_t workspace_bytes, void *stream);
+
+/* Router logits alone (MoeSpec `wr`, `router_bias`): x [T, H] -> logits
+ * [T, E] f32 = x . Wr + Br with f32 accumulation.  Needs router_weight bound
+ * and moe_workspace_size(T) bytes of workspace.
+ * Errors: INVALID_ARGUMENT, SHAPE_MISMATCH, UNBOUND, UNSUPPORTED, WORKSPACE, HIP. */
+moe_status moe_router_logits(const moe_layer *layer, const moe_tensor *x, moe_tensor *logits,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /* Release the handle (~QMoEWoQ).  Never frees caller buffers.  NULL is a no-op. */
 moe_status moe_destroy(moe_layer *layer);

@@ -22,13 +22,15 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_SHAPE_MI
                 5: "MOE_ERR_UNSUPPORTED", 6: "MOE_ERR_WORKSPACE", 7: "MOE_ERR_HIP"}
 MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_MXFP4, MOE_DTYPE_I32 = 0, 1, 2, 3
 SCORING = {"softmax": 0, "sigmoid": 1}
-ACTIVATION = {"silu": 0, "swiglu_clamped": 1}
+ACTIVATION = {"silu": 0, "swiglu_clamped": 1, "relu": 2, "gelu": 3, "silu_plain": 4,
+              "identity": 5}
+GELU_MODE = {"erf": 0, "tanh": 1}
 FUSION = {"unfused": 0, "interleaved": 1, "split": 2}
 WDTYPE = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16, "mxfp4": MOE_DTYPE_MXFP4}
 
 EXPORTS = ["moe_options_default", "moe_create", "moe_set_weights", "moe_prepare",
            "moe_workspace_size", "moe_forward", "moe_forward_timed", "moe_route",
-           "moe_destroy", "moe_last_error", "moe_status_string"]
+           "moe_router_logits", "moe_destroy", "moe_last_error", "moe_status_string"]
 MOE_STAGE_EVENTS = 6
 
 
@@ -38,7 +40,8 @@ class moe_options(C.Structure):
                 ("routed_scaling_factor", C.c_float), ("activation", C.c_int32),
                 ("swiglu_fusion", C.c_int32), ("swiglu_alpha", C.c_float),
                 ("swiglu_beta", C.c_float), ("swiglu_limit", C.c_float),
-                ("gemm_variant", C.c_int32)]
+                ("gemm_variant", C.c_int32), ("gelu_mode", C.c_int32),
+                ("weigh_inputs", C.c_int32)]
 
 
 class moe_tensor(C.Structure):
@@ -49,7 +52,8 @@ class moe_tensor(C.Structure):
 class moe_weights(C.Structure):
     _fields_ = [(n, moe_tensor) for n in (
         "gate_up_experts", "down_experts", "gate_experts", "gate_up_bias",
-        "down_bias", "gate_bias", "e_score_correction_bias")]
+        "down_bias", "gate_bias", "e_score_correction_bias", "router_weight",
+        "router_bias")]
 
 
 class moe_routing_out(C.Structure):
@@ -93,6 +97,8 @@ def lib():
                                    C.POINTER(P)], C.c_int),
             "moe_route": ([P, C.POINTER(moe_tensor), C.POINTER(moe_routing_out), P,
                            C.c_size_t, P], C.c_int),
+            "moe_router_logits": ([P, C.POINTER(moe_tensor), C.POINTER(moe_tensor), P,
+                                   C.c_size_t, P], C.c_int),
             "moe_destroy": ([P], C.c_int),
             "moe_last_error": ([], C.c_char_p),
             "moe_status_string": ([C.c_int], C.c_char_p),
@@ -114,7 +120,8 @@ def options(**kw) -> moe_options:
     """moe_options from the defaults, overridden by clika-style kwargs
     (scoring/routing_mode, renormalize, n_group, topk_group,
     routed_scaling_factor, activation, swiglu_fusion, swiglu_alpha,
-    swiglu_beta, swiglu_limit, gemm_variant)."""
+    swiglu_beta, swiglu_limit, gemm_variant, gelu_mode,
+    weigh_inputs / apply_router_weight_on_input)."""
     o = moe_options()
     check(lib().moe_options_default(C.byref(o)))
     for k, v in kw.items():
@@ -125,6 +132,10 @@ def options(**kw) -> moe_options:
             v = ACTIVATION[v]
         elif k == "swiglu_fusion" and isinstance(v, str):
             v = FUSION[v]
+        elif k == "gelu_mode" and isinstance(v, str):
+            v = GELU_MODE[v]
+        elif k == "apply_router_weight_on_input":
+            k = "weigh_inputs"
         setattr(o, k, int(v) if isinstance(v, bool) else v)
     return o
 

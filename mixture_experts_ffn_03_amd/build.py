@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libmoe_mi355x.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "gemm_f32.hip",
-           "combine.hip"]
+           "combine.hip", "router.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -34,6 +34,9 @@ struct moe_layer {
     mutable int down_f16_ok;
     mutable uint8_t *mx_pack = nullptr;
     mutable int64_t mx_off[4] = {0, 0, 0, 0};   // codes 1, scales 1, codes 2, scales 2
+    // the bound router transposed to [E, H] (rows K-contiguous, like the
+    // expert stacks) for the router GEMM; made at prepare, freed by destroy
+    mutable void *wr_t = nullptr;
 };
 
 namespace {
@@ -94,9 +97,28 @@ int act_dtype(const moe_layer *l)
     return l->wdtype == MOE_DTYPE_F32 ? MOE_DTYPE_F32 : MOE_DTYPE_BF16;
 }
 
+// Gated activations read a gate and an up projection (ONNX MoE fusion_size
+// 2 when fused); the others one fc1 projection [E, I, H].
+bool gated(const moe_layer *l)
+{
+    return l->opts.activation == MOE_ACT_SILU_GATED ||
+           l->opts.activation == MOE_ACT_SWIGLU_CLAMPED;
+}
+
 bool fused(const moe_layer *l)
 {
-    return l->opts.swiglu_fusion != MOE_FUSION_NONE;
+    return gated(l) && l->opts.swiglu_fusion != MOE_FUSION_NONE;
+}
+
+// gate and up in two stacks (gated, swiglu_fusion NONE)
+bool two_stacks(const moe_layer *l)
+{
+    return gated(l) && l->opts.swiglu_fusion == MOE_FUSION_NONE;
+}
+
+bool has_router(const moe_layer *l)
+{
+    return present(l->w.router_weight);
 }
 
 moe_status check_bound(const moe_layer *l)
@@ -104,12 +126,12 @@ moe_status check_bound(const moe_layer *l)
     if (!l->bound) return fail(MOE_ERR_UNBOUND, "weights not bound (call moe_set_weights)");
     if (!present(l->w.gate_up_experts) || !present(l->w.down_experts))
         return fail(MOE_ERR_UNBOUND, "gate_up_experts / down_experts slot unbound");
-    if (!fused(l) && !present(l->w.gate_experts))
+    if (two_stacks(l) && !present(l->w.gate_experts))
         return fail(MOE_ERR_UNBOUND, "gate_experts slot unbound (swiglu_fusion = NONE)");
     if (l->has_gu_bias) {
         if (!present(l->w.gate_up_bias))
             return fail(MOE_ERR_UNBOUND, "declared gate_up_bias slot unbound");
-        if (!fused(l) && !present(l->w.gate_bias))
+        if (two_stacks(l) && !present(l->w.gate_bias))
             return fail(MOE_ERR_UNBOUND, "declared gate_bias slot unbound");
     }
     if (l->has_d_bias && !present(l->w.down_bias))
@@ -125,7 +147,7 @@ size_t align256(size_t v)
 // Workspace carving.  Every region starts on a 256-byte boundary.
 struct Workspace {
     size_t ids, weights, block_counts, block_base, counts, offsets, tile_cum1, tile_cum2,
-        row_token, slot_row, hfmt, h, y, total;
+        row_token, slot_row, row_weight, logits, router_grp, hfmt, h, y, total;
 };
 
 int64_t max_m_tiles_of(const moe_layer *l, int64_t T, int bm)
@@ -156,6 +178,9 @@ Workspace layout(const moe_layer *l, int64_t T)
     w.tile_cum2 = take((l->E + 1) * 4);
     w.row_token = take(TK * 4);
     w.slot_row = take(TK * 4);
+    w.row_weight = take(TK * 4);          // weigh-inputs: routing weight per row
+    w.logits = take(T * l->E * 4);        // router logits when the layer's router runs
+    w.router_grp = take(8 * 4);           // router GEMM: counts, offsets, tile_cum
     // one h-format byte per (GEMM-1 M-tile, GEMM-1 feature tile), worst case
     // over the two 16-bit kernel variants
     size_t nfmt = 0;
@@ -269,11 +294,45 @@ moe_status run_route(const moe_layer *l, const float *logits, int64_t T, char *w
     pa.tile_cum2 = (int32_t *)(ws + W.tile_cum2);
     pa.bm1 = path_bm(path);
     pa.bm2 = path_bm(path);
+    pa.weights = ra.weights;
+    pa.row_weight = l->opts.weigh_inputs ? (float *)(ws + W.row_weight) : nullptr;
     if ((st = hip_check(launch_permute(pa, s), "permute launch"))) return st;
     if (events && events[2] &&
         (st = hip_check(hipEventRecord((hipEvent_t)events[2], s), "event record")))
         return st;
     return MOE_OK;
+}
+
+// Router logits [T, E] f32 = x . Wr + Br ("MoeSpec" wr, router_bias): the
+// grouped GEMM as one group of T rows against the transposed router.
+moe_status run_router(const moe_layer *l, const void *x, int64_t T, float *logits, char *ws,
+                      const Workspace &W, Path path, hipStream_t s)
+{
+    GemmArgs g{};
+    int32_t *grp = (int32_t *)(ws + W.router_grp);
+    g.a = x;
+    g.row_token = nullptr;
+    g.counts = grp;
+    g.offsets = grp + 1;
+    g.tile_cum = grp + 3;
+    g.E = 1;
+    g.Kd = (int)l->H;
+    g.Nout = (int)l->E;
+    const int bm = path_bm(path), bn = path_bn(path, false);
+    g.nN = (int)((l->E + bn - 1) / bn);
+    g.out = logits;
+    g.w.w_gate = g.w.w_up = l->wr_t;
+    g.w.e_rows = l->E;
+    g.w.row_mul = 1;
+    if (present(l->w.router_bias)) g.w.b_gate = l->w.router_bias.data;
+    moe_status st = hip_check(launch_single_group(grp, grp + 1, grp + 3, (int)T, bm, s),
+                              "router setup launch");
+    if (st) return st;
+    const int64_t m_tiles = (T + bm - 1) / bm;
+    if (path == Path::kF32)
+        return hip_check(launch_gemm_f32(kEpiPlain, g, m_tiles, s), "router launch");
+    return hip_check(launch_gemm_bf16(kind_of(path), kEpiPlain, false, g, m_tiles, s),
+                     "router launch");
 }
 
 moe_status copy_routing(const moe_layer *l, int64_t T, const char *ws, const Workspace &W,
@@ -323,7 +382,8 @@ moe_status check_workspace(const moe_layer *l, int64_t T, void *ws, size_t bytes
 moe_status pack_mxfp4(const moe_layer *l, hipStream_t s)
 {
     const int64_t E = l->E, H = l->H, I = l->I;
-    const int64_t sz[4] = {mx_pack_bytes(2, I, H, E), mx_pack_scale_bytes(2, I, H, E),
+    const int ops1 = gated(l) ? 2 : 1;
+    const int64_t sz[4] = {mx_pack_bytes(ops1, I, H, E), mx_pack_scale_bytes(ops1, I, H, E),
                            mx_pack_bytes(1, H, I, E), mx_pack_scale_bytes(1, H, I, E)};
     if (!l->mx_pack) {
         int64_t total = 0;
@@ -338,11 +398,18 @@ moe_status pack_mxfp4(const moe_layer *l, hipStream_t s)
     }
     PackArgs a{};
     a.E = (int)E;
-    a.ops = 2;
+    a.ops = ops1;
     a.Nh = (int)I;
     a.K = (int)H;
     a.nks = (int)((H + 63) / 64);
-    if (fused(l)) {
+    if (!gated(l)) {
+        // one fc1 stack [E, I, H]
+        a.codes[0] = a.codes[1] = (const uint8_t *)l->w.gate_up_experts.data;
+        a.scales[0] = a.scales[1] = l->w.gate_up_experts.scales;
+        a.e_rows = I;
+        a.row_mul = 1;
+        a.off[0] = a.off[1] = 0;
+    } else if (fused(l)) {
         a.codes[0] = a.codes[1] = (const uint8_t *)l->w.gate_up_experts.data;
         a.scales[0] = a.scales[1] = l->w.gate_up_experts.scales;
         a.e_rows = 2 * I;
@@ -387,6 +454,18 @@ moe_status prepare_locked(const moe_layer *l, hipStream_t s)
         moe_status st = pack_mxfp4(l, s);
         if (st) return st;
     }
+    if (has_router(l)) {
+        const int eb = act_dtype(l) == MOE_DTYPE_F32 ? 4 : 2;
+        if (!l->wr_t) {
+            moe_status st = hip_check(hipMalloc(&l->wr_t, (size_t)(l->E * l->H * eb)),
+                                      "router alloc");
+            if (st) return st;
+        }
+        moe_status st = hip_check(launch_transpose(l->w.router_weight.data, l->wr_t, (int)l->H,
+                                                   (int)l->E, eb, s),
+                                  "router transpose");
+        if (st) return st;
+    }
     if (l->wdtype != MOE_DTYPE_F32) {
         uint32_t *d = nullptr;
         moe_status st = hip_check(hipMalloc((void **)&d, 16), "prepare alloc");
@@ -404,6 +483,11 @@ moe_status prepare_locked(const moe_layer *l, hipStream_t s)
         (void)hipFree(d);
         if ((st = hip_check(e, "prepare weight scan"))) return st;
         ok = mx ? (r[1] >= 104u && r[2] <= 140u) : (r[0] <= 0x477fu);
+    }
+    if (l->wdtype == MOE_DTYPE_F32 && has_router(l)) {
+        // (the 16-bit path synchronised in its weight scan)
+        moe_status st = hip_check(hipStreamSynchronize(s), "prepare sync");
+        if (st) return st;
     }
     l->down_f16_ok = ok;
     l->prepared = true;
@@ -470,8 +554,12 @@ moe_status moe_create(int64_t E, int64_t H, int64_t I, int64_t K, moe_dtype wdty
             return fail(MOE_ERR_INVALID_ARGUMENT,
                         "top_k exceeds the experts of topk_group groups");
     }
-    if (o.activation != MOE_ACT_SILU_GATED && o.activation != MOE_ACT_SWIGLU_CLAMPED)
+    if (o.activation < MOE_ACT_SILU_GATED || o.activation > MOE_ACT_IDENTITY)
         return fail(MOE_ERR_INVALID_ARGUMENT, "unknown activation %d", o.activation);
+    if (o.gelu_mode != MOE_GELU_ERF && o.gelu_mode != MOE_GELU_TANH)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "unknown gelu_mode %d", o.gelu_mode);
+    if (o.weigh_inputs != 0 && o.weigh_inputs != 1)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "weigh_inputs must be 0 or 1");
     if (o.swiglu_fusion < MOE_FUSION_NONE || o.swiglu_fusion > MOE_FUSION_SPLIT)
         return fail(MOE_ERR_INVALID_ARGUMENT, "unknown swiglu_fusion %d", o.swiglu_fusion);
     if (o.gemm_variant < 0 || o.gemm_variant > 3)
@@ -500,16 +588,17 @@ moe_status moe_set_weights(moe_layer *l, const moe_weights *w)
     if (!l || !w) return fail(MOE_ERR_INVALID_ARGUMENT, "layer or weights is NULL");
     const int64_t E = l->E, H = l->H, I = l->I;
     const int wd = l->wdtype, ad = act_dtype(l);
-    const bool fz = fused(l);
+    const bool fz = fused(l), two = two_stacks(l);
     moe_status st;
     if (!present(w->gate_up_experts) || !present(w->down_experts))
         return fail(MOE_ERR_SHAPE_MISMATCH, "gate_up_experts and down_experts are required");
     if ((st = check_tensor("gate_up_experts", w->gate_up_experts, wd, {E, fz ? 2 * I : I, H})))
         return st;
     if ((st = check_tensor("down_experts", w->down_experts, wd, {E, H, I}))) return st;
-    if (fz && present(w->gate_experts))
-        return fail(MOE_ERR_SHAPE_MISMATCH, "gate_experts given for a fused gate||up layout");
-    if (!fz) {
+    if (!two && present(w->gate_experts))
+        return fail(MOE_ERR_SHAPE_MISMATCH, fz ? "gate_experts given for a fused gate||up layout"
+                                               : "gate_experts given for a non-gated activation");
+    if (two) {
         if (!present(w->gate_experts))
             return fail(MOE_ERR_SHAPE_MISMATCH,
                         "gate_experts is required when swiglu_fusion = NONE");
@@ -524,8 +613,9 @@ moe_status moe_set_weights(moe_layer *l, const moe_weights *w)
     if (present(w->gate_bias)) {
         if (!l->has_gu_bias)
             return fail(MOE_ERR_NOT_DECLARED, "gate_bias given but not declared");
-        if (fz)
-            return fail(MOE_ERR_SHAPE_MISMATCH, "gate_bias given for a fused gate||up layout");
+        if (!two)
+            return fail(MOE_ERR_SHAPE_MISMATCH,
+                        "gate_bias given without a separate gate stack");
         if ((st = check_tensor("gate_bias", w->gate_bias, ad, {E, I}))) return st;
     }
     if (present(w->down_bias)) {
@@ -537,6 +627,16 @@ moe_status moe_set_weights(moe_layer *l, const moe_weights *w)
         (st = check_tensor("e_score_correction_bias", w->e_score_correction_bias,
                            MOE_DTYPE_F32, {E})))
         return st;
+    // the layer's own router ("MoeSpec" wr [H, E], router_bias [E]); binds
+    // whatever was declared, like the selection bias
+    if (present(w->router_weight) &&
+        (st = check_tensor("router_weight", w->router_weight, ad, {H, E})))
+        return st;
+    if (present(w->router_bias)) {
+        if (!present(w->router_weight))
+            return fail(MOE_ERR_SHAPE_MISMATCH, "router_bias given without router_weight");
+        if ((st = check_tensor("router_bias", w->router_bias, ad, {E}))) return st;
+    }
     std::lock_guard<std::mutex> lock(l->mu);
     l->w = *w;
     l->bound = true;
@@ -593,9 +693,14 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
                              size_t ws_bytes, moe_routing_out *routing, void *stream,
                              void *const *events)
 {
-    if (!l || !x || !logits || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (!l || !x || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL argument");
     moe_status st = check_bound(l);
     if (st) return st;
+    // no logits: the layer's bound router computes them
+    // (absent means NULL or ndim 0: an empty [0, E] tensor may have no data)
+    const bool own_router = !logits || logits->ndim == 0;
+    if (own_router && !has_router(l))
+        return fail(MOE_ERR_UNBOUND, "router_logits not given and no router_weight bound");
     const int ad = act_dtype(l);
     if (x->dtype != MOE_DTYPE_F32 && x->dtype != MOE_DTYPE_BF16)
         return fail(MOE_ERR_SHAPE_MISMATCH, "x dtype must be f32 or bf16");
@@ -605,11 +710,13 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     bool okT;
     const int64_t T = tokens_of(*x, l->H, &okT);
     if (!okT) return fail(MOE_ERR_SHAPE_MISMATCH, "x must be [T, H] or [B, S, H]");
-    bool okL;
-    const int64_t TL = tokens_of(*logits, l->E, &okL);
-    if (!okL || TL != T || logits->dtype != MOE_DTYPE_F32)
-        return fail(MOE_ERR_SHAPE_MISMATCH, "router_logits must be f32 [T, E] with T = %lld",
-                    (long long)T);
+    if (!own_router) {
+        bool okL;
+        const int64_t TL = tokens_of(*logits, l->E, &okL);
+        if (!okL || TL != T || logits->dtype != MOE_DTYPE_F32)
+            return fail(MOE_ERR_SHAPE_MISMATCH,
+                        "router_logits must be f32 [T, E] with T = %lld", (long long)T);
+    }
     auto same_as_x = [&](const moe_tensor &t) {
         if (t.dtype != x->dtype || t.ndim != x->ndim) return false;
         for (int i = 0; i < x->ndim; ++i)
@@ -622,7 +729,7 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
         return fail(MOE_ERR_SHAPE_MISMATCH, "shared_output must match x's shape and dtype");
     if (T > (1 << 24)) return fail(MOE_ERR_INVALID_ARGUMENT, "T out of range");
     if (T == 0) return MOE_OK;
-    if (!x->data || !logits->data || !out->data)
+    if (!x->data || !out->data || (!own_router && !logits->data))
         return fail(MOE_ERR_INVALID_ARGUMENT, "x, router_logits or out data is NULL");
     Workspace W;
     if ((st = check_workspace(l, T, ws, ws_bytes, &W))) return st;
@@ -637,7 +744,10 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     };
     const Path path = choose_path(l, T);
     if ((st = mark(0))) return st;
-    if ((st = run_route(l, (const float *)logits->data, T, wsb, W, path, s, events))) return st;
+    const float *lg = own_router ? (const float *)(wsb + W.logits) : (const float *)logits->data;
+    if (own_router && (st = run_router(l, x->data, T, (float *)(wsb + W.logits), wsb, W, path, s)))
+        return st;
+    if ((st = run_route(l, lg, T, wsb, W, path, s, events))) return st;
 
     const int bm = path_bm(path);
     const int64_t max_m_tiles = max_m_tiles_of(l, T, bm);
@@ -654,10 +764,14 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     g1.E = (int)l->E;
     g1.Kd = (int)l->H;
     g1.Nout = (int)l->I;
-    const int bn1 = path_bn(path, true);
+    const bool gt = gated(l);
+    const int epi1 = gt ? kEpiGated : kEpiAct;
+    const int bn1 = path_bn(path, gt);
     g1.nN = (int)((l->I + bn1 - 1) / bn1);
     g1.out = wsb + W.h;
     g1.act = l->opts.activation;
+    g1.gelu_mode = l->opts.gelu_mode;
+    g1.row_w = l->opts.weigh_inputs ? (const float *)(wsb + W.row_weight) : nullptr;
     g1.alpha = l->opts.swiglu_alpha;
     g1.beta = l->opts.swiglu_beta;
     g1.limit = l->opts.swiglu_limit;
@@ -666,7 +780,15 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     g1.h_width = bn1;
     g1.f16_ok = l->down_f16_ok;
     WeightRows &w1 = g1.w;
-    if (fz) {
+    if (!gt) {
+        // one fc1 stack [E, I, H] and its bias [E, I]
+        w1.w_gate = w1.w_up = l->w.gate_up_experts.data;
+        w1.s_gate = w1.s_up = l->w.gate_up_experts.scales;
+        w1.e_rows = l->I;
+        w1.row_mul = 1;
+        w1.off_gate = w1.off_up = 0;
+        if (present(l->w.gate_up_bias)) w1.b_gate = l->w.gate_up_bias.data;
+    } else if (fz) {
         w1.w_gate = w1.w_up = l->w.gate_up_experts.data;
         w1.s_gate = w1.s_up = l->w.gate_up_experts.scales;
         w1.e_rows = 2 * l->I;
@@ -729,15 +851,16 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
         return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch");
 
     if (path == Path::kF32) {
-        if ((st = hip_check(launch_gemm_f32(true, g1, max_m_tiles, s), "gemm1 launch"))) return st;
+        if ((st = hip_check(launch_gemm_f32(epi1, g1, max_m_tiles, s), "gemm1 launch"))) return st;
         if ((st = mark(3))) return st;
-        if ((st = hip_check(launch_gemm_f32(false, g2, max_m_tiles, s), "gemm2 launch"))) return st;
+        if ((st = hip_check(launch_gemm_f32(kEpiDown, g2, max_m_tiles, s), "gemm2 launch")))
+            return st;
     } else {
         const GemmKind kind = kind_of(path);
-        if ((st = hip_check(launch_gemm_bf16(kind, true, mx, g1, max_m_tiles, s), "gemm1 launch")))
+        if ((st = hip_check(launch_gemm_bf16(kind, epi1, mx, g1, max_m_tiles, s), "gemm1 launch")))
             return st;
         if ((st = mark(3))) return st;
-        if ((st = hip_check(launch_gemm_bf16(kind, false, mx, g2, max_m_tiles, s),
+        if ((st = hip_check(launch_gemm_bf16(kind, kEpiDown, mx, g2, max_m_tiles, s),
                             "gemm2 launch")))
             return st;
     }
@@ -753,14 +876,44 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     ca.H = (int)l->H;
     ca.K = (int)l->K;
     ca.out_bf16 = x->dtype == MOE_DTYPE_BF16;
+    ca.unit_weights = l->opts.weigh_inputs;
     if ((st = hip_check(launch_combine(ca, s), "combine launch"))) return st;
     if ((st = mark(5))) return st;
     return copy_routing(l, T, wsb, W, routing, s);
 }
 
+moe_status moe_router_logits(const moe_layer *l, const moe_tensor *x, moe_tensor *logits,
+                             void *ws, size_t ws_bytes, void *stream)
+{
+    if (!l || !x || !logits) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL argument");
+    moe_status st = check_bound(l);
+    if (st) return st;
+    if (!has_router(l)) return fail(MOE_ERR_UNBOUND, "router_weight slot unbound");
+    if (x->dtype != act_dtype(l))
+        return fail(MOE_ERR_UNSUPPORTED, "x dtype %s with %s weights", dtype_name(x->dtype),
+                    dtype_name(l->wdtype));
+    bool okT, okL;
+    const int64_t T = tokens_of(*x, l->H, &okT);
+    if (!okT) return fail(MOE_ERR_SHAPE_MISMATCH, "x must be [T, H] or [B, S, H]");
+    const int64_t TL = tokens_of(*logits, l->E, &okL);
+    if (!okL || TL != T || logits->dtype != MOE_DTYPE_F32)
+        return fail(MOE_ERR_SHAPE_MISMATCH, "logits must be f32 [T, E] with T = %lld",
+                    (long long)T);
+    if (T > (1 << 24)) return fail(MOE_ERR_INVALID_ARGUMENT, "T out of range");
+    if (T == 0) return MOE_OK;
+    if (!x->data || !logits->data)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "x or logits data is NULL");
+    Workspace W;
+    if ((st = check_workspace(l, T, ws, ws_bytes, &W))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = prepare_locked(l, s))) return st;
+    return run_router(l, x->data, T, (float *)logits->data, (char *)ws, W, choose_path(l, T), s);
+}
+
 moe_status moe_destroy(moe_layer *l)
 {
     if (l && l->mx_pack) (void)hipFree(l->mx_pack);
+    if (l && l->wr_t) (void)hipFree(l->wr_t);
     delete l;
     return MOE_OK;
 }

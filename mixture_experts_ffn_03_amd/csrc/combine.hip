@@ -1,6 +1,8 @@
 // Router-weighted combine (clika "MoE": the expert outputs combine under the
 // router weights; "ClikaRT::nn::QMoEWoQ::forward": an optional shared-expert
-// output folds into the same epilogue).
+// output folds into the same epilogue).  With weigh-inputs routing
+// ("MoeSpec" `weigh_inputs`) the weights were applied to the experts' inputs
+// and every kept output joins the sum with weight one.
 //
 // out[t, :] = sum_{j=0..K-1} w[t, j] * y[slot_row[t, j], :]  (+ shared[t, :])
 // accumulated in f32 in slot order j = 0, 1, ..., rounded once to the output
@@ -22,7 +24,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     const int t = (int)(idx / H4), c = (int)(idx % H4) * 4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < a.K; ++j) {
-        const float w = a.weights[(int64_t)t * a.K + j];
+        const float w = a.unit_weights ? 1.0f : a.weights[(int64_t)t * a.K + j];
         const int row = a.slot_row[(int64_t)t * a.K + j];
         const f32x4 v = *(const f32x4 *)(a.y + (int64_t)row * a.H + c);
         acc += w * v;

@@ -110,46 +110,61 @@ __device__ inline f32x16 mfma(const u32x4 &a, const u32x4 &b, const f32x16 &c)
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Epilogue shared by both GEMM kernels: lane holds output features
-// 8*i4 + 4*(lane/32) + j (j = 0..3) of token lane % 32 of each 32x32 block.
-template <class TL, bool GATED>
+// Epilogue: lane holds output features 8*i4 + 4*(lane/32) + j (j = 0..3) of
+// token lane % 32 of each 32x32 block.
+//  gated / act: (weigh-inputs: times the row's routing weight) + fc1 bias,
+//      activation, then h stored in fp16 when the tile's max |h| fits fp16
+//      and the down weights convert exactly, else bf16 (format byte per tile);
+//  down / plain: + bias, f32 store.
+template <class TL, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
                                          f32x16 (&acc)[TL::FN][TL::FM], float *s_red)
 {
     constexpr int NWAVES = TL::NT / 64;
+    constexpr bool GATED = EPI == kEpiGated;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave % TL::WN, wm = wave / TL::WN;
     const int lrow = lane & 31;
     const int fq = (lane >> 5) * 4;
-    if (GATED) {
-        // pass 1: activation into the gate accumulators, tile max |h|
+    if constexpr (EPI == kEpiGated || EPI == kEpiAct) {
+        // features of the h tile held per wave: gate/up pairs, or every block
+        constexpr int FH = GATED ? TL::FN / 2 : TL::FN;
+        constexpr int WH = GATED ? TL::TN / 2 : TL::TN;
+        // pass 1: activation into the (gate) accumulators, tile max |h|
         const int64_t eb = (int64_t)tw.e * g.w.e_rows;
         float hmax = 0.0f;
 #pragma unroll
-        for (int fp = 0; fp < TL::FN / 2; ++fp)
+        for (int m = 0; m < TL::FM; ++m) {
+            const int tl = wm * TL::TM + m * 32 + lrow;
+            const bool tok_ok = tl < tw.nrows;
+            const float rs = (g.row_w && tok_ok) ? g.row_w[tw.row0 + tl] : 1.0f;
 #pragma unroll
-            for (int m = 0; m < TL::FM; ++m) {
-                const bool tok_ok = wm * TL::TM + m * 32 + lrow < tw.nrows;
+            for (int fp = 0; fp < FH; ++fp)
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
-                    const int c = tw.n0 + wn * (TL::TN / 2) + fp * 32 + i4 * 8 + fq;
+                    const int c = tw.n0 + wn * WH + fp * 32 + i4 * 8 + fq;
                     const bool ok = tok_ok && c < g.Nout;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        float gv = acc[fp][m][i4 * 4 + j];
-                        float uv = acc[fp + TL::FN / 2][m][i4 * 4 + j];
+                        float gv = acc[fp][m][i4 * 4 + j] * rs;
                         if (ok && g.w.b_gate)
                             gv += bias_at(g.w.b_gate,
                                           eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_gate);
-                        if (ok && g.w.b_up)
-                            uv += bias_at(g.w.b_up,
-                                          eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_up);
-                        const float h = gated_act(g.act, gv, uv, g.alpha, g.beta, g.limit);
+                        float h;
+                        if constexpr (GATED) {
+                            float uv = acc[fp + TL::FN / 2][m][i4 * 4 + j] * rs;
+                            if (ok && g.w.b_up)
+                                uv += bias_at(g.w.b_up,
+                                              eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_up);
+                            h = gated_act(g.act, gv, uv, g.alpha, g.beta, g.limit);
+                        } else {
+                            h = single_act(g.act, g.gelu_mode, gv);
+                        }
                         acc[fp][m][i4 * 4 + j] = h;
                         if (ok) hmax = fmaxf(hmax, fabsf(h));
                     }
                 }
-            }
+        }
         // block max -> storage format of this h tile
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, off, 64));
@@ -163,7 +178,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
         // pass 2: store h
         uint16_t *h = (uint16_t *)g.out;
 #pragma unroll
-        for (int fp = 0; fp < TL::FN / 2; ++fp)
+        for (int fp = 0; fp < FH; ++fp)
 #pragma unroll
             for (int m = 0; m < TL::FM; ++m) {
                 const int tl = wm * TL::TM + m * 32 + lrow;
@@ -171,7 +186,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
                 uint16_t *hrow = h + (int64_t)(tw.row0 + tl) * g.Nout;
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
-                    const int c = tw.n0 + wn * (TL::TN / 2) + fp * 32 + i4 * 8 + fq;
+                    const int c = tw.n0 + wn * WH + fp * 32 + i4 * 8 + fq;
                     if (c >= g.Nout) continue;
                     const f32x16 &a = acc[fp][m];
                     const int r0 = i4 * 4;
@@ -329,10 +344,12 @@ __device__ const u32x4 g_zero16 = {0u, 0u, 0u, 0u};
 
 // RAGGED: the reduction length is not a multiple of BK (the last k-step's
 // token chunks past it read zeros); otherwise no k-step needs a bounds test.
-template <class TL, bool GATED, bool F16, bool RAGGED>
+template <class TL, int EPI, bool F16, bool RAGGED>
 __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, uint8_t *lds,
                                          float *s_red)
 {
+    constexpr bool GATED = EPI == kEpiGated;
+    constexpr bool HIN = EPI == kEpiDown;    // A operand is h with per-tile formats
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Kd = g.Kd;
 
@@ -444,7 +461,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
 
     // h formats of these rows (bf16 down GEMM only; read from global memory,
     // whose waits only ever lengthen the explicit ones)
-    const uint8_t *hf = GATED ? nullptr : g.hfmt + (int64_t)tw.mg * g.h_tiles;
+    const uint8_t *hf = HIN ? g.hfmt + (int64_t)tw.mg * g.h_tiles : nullptr;
 
     f32x16 acc[TL::FN][TL::FM];
 #pragma unroll
@@ -493,7 +510,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
             // token chunk of this sub-step (MXFP4: the permuted k order)
             const int acoff = ((TL::MX ? 4 * lhalf + ks : ks * 2 + lhalf) ^ lsw) * 16;
             // bf16 down GEMM: an fp16-stored h step is rounded to bf16
-            const bool a_f16 = !GATED && !F16 && hf[(kt * TL::BK) / g.h_width] == kHF16;
+            const bool a_f16 = HIN && !F16 && hf[(kt * TL::BK) / g.h_width] == kHF16;
 #pragma unroll
             for (int m = 0; m < MV; ++m) {
                 af[b][m] = *(const u32x4 *)(sa + (wm * TL::TM + m * 32 + lrow) * TL::ROWB + acoff);
@@ -581,15 +598,15 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     else kloop(std::integral_constant<int, 0>{});
     // all waves are done reading LDS before the epilogue reuses it as scratch
     __syncthreads();
-    epilogue<TL, GATED>(g, tw, acc, s_red);
+    epilogue<TL, EPI>(g, tw, acc, s_red);
 }
 
 // At least two waves per SIMD (256 VGPRs each): the 4-wave MXFP4 mid tile
 // then runs two workgroups per CU.
-template <class TL, bool GATED>
+template <class TL, int EPI>
 __global__ __launch_bounds__(TL::NT, 2) void gemm_dma_kernel(GemmArgs g)
 {
-    constexpr int NW = GATED ? TL::BN / 2 : TL::BN;
+    constexpr int NW = EPI == kEpiGated ? TL::BN / 2 : TL::BN;
     // one LDS allocation: the scheduling table, then the stages, then the
     // epilogue scratch use it in turn
     __shared__ __attribute__((aligned(1024))) uint8_t lds[TL::LDS_BYTES];
@@ -598,8 +615,8 @@ __global__ __launch_bounds__(TL::NT, 2) void gemm_dma_kernel(GemmArgs g)
 
     TileWork tw;
     if (!find_tile(g, s_cum, TL::BM, NW, &tw)) return;
-    bool f16 = false;
-    if (!GATED) {
+    const bool ragged = g.Kd % TL::BK != 0;
+    if constexpr (EPI == kEpiDown) {
         // down GEMM: fp16 operands iff every h tile of these rows is fp16
         const uint8_t *hf = g.hfmt + (int64_t)tw.mg * g.h_tiles;
         int all16 = g.f16_ok;
@@ -612,32 +629,40 @@ __global__ __launch_bounds__(TL::NT, 2) void gemm_dma_kernel(GemmArgs g)
         __syncthreads();
         if (!all16) *flag = 0;
         __syncthreads();
-        f16 = *flag != 0;
+        const bool f16 = *flag != 0;
         __syncthreads();                     // before the loads overwrite it
+        if (f16) {
+            if (ragged) dma_body<TL, EPI, true, true>(g, tw, lds, s_red);
+            else dma_body<TL, EPI, true, false>(g, tw, lds, s_red);
+        } else {
+            if (ragged) dma_body<TL, EPI, false, true>(g, tw, lds, s_red);
+            else dma_body<TL, EPI, false, false>(g, tw, lds, s_red);
+        }
     } else {
         __syncthreads();                     // every s_cum read is done
-    }
-    const bool ragged = g.Kd % TL::BK != 0;
-    if constexpr (GATED) {
-        if (ragged) dma_body<TL, true, false, true>(g, tw, lds, s_red);
-        else dma_body<TL, true, false, false>(g, tw, lds, s_red);
-    } else {
-        if (f16) {
-            if (ragged) dma_body<TL, false, true, true>(g, tw, lds, s_red);
-            else dma_body<TL, false, true, false>(g, tw, lds, s_red);
-        } else {
-            if (ragged) dma_body<TL, false, false, true>(g, tw, lds, s_red);
-            else dma_body<TL, false, false, false>(g, tw, lds, s_red);
-        }
+        if (ragged) dma_body<TL, EPI, false, true>(g, tw, lds, s_red);
+        else dma_body<TL, EPI, false, false>(g, tw, lds, s_red);
     }
 }
 
-template <class TL, bool GATED>
+template <class TL, int EPI>
 hipError_t launch_dma(const GemmArgs &a, int64_t max_m_tiles, hipStream_t s)
 {
     const int64_t grid = max_m_tiles * a.nN + 8;
-    gemm_dma_kernel<TL, GATED><<<dim3((unsigned)grid), dim3(TL::NT), 0, s>>>(a);
+    gemm_dma_kernel<TL, EPI><<<dim3((unsigned)grid), dim3(TL::NT), 0, s>>>(a);
     return hipGetLastError();
+}
+
+// every epilogue mode of one tile shape
+template <class TL>
+hipError_t launch_epi(int epi, const GemmArgs &a, int64_t max_m_tiles, hipStream_t s)
+{
+    switch (epi) {
+    case kEpiGated: return launch_dma<TL, kEpiGated>(a, max_m_tiles, s);
+    case kEpiAct: return launch_dma<TL, kEpiAct>(a, max_m_tiles, s);
+    case kEpiPlain: return launch_dma<TL, kEpiPlain>(a, max_m_tiles, s);
+    default: return launch_dma<TL, kEpiDown>(a, max_m_tiles, s);
+    }
 }
 
 // ---- prepare-time range scan of a down-weight stack
@@ -738,28 +763,21 @@ int gemm_bn(GemmKind kind, bool gated)
     return gated ? bn / 2 : bn;
 }
 
-hipError_t launch_gemm_bf16(GemmKind kind, bool gated, bool mxfp4, const GemmArgs &a,
+hipError_t launch_gemm_bf16(GemmKind kind, int epi, bool mxfp4, const GemmArgs &a,
                             int64_t max_m_tiles, hipStream_t s)
 {
-    if (kind == GemmKind::kPrefill) {
-        if (mxfp4)
-            return gated ? launch_dma<PrefillMXTile, true>(a, max_m_tiles, s)
-                         : launch_dma<PrefillMXTile, false>(a, max_m_tiles, s);
-        return gated ? launch_dma<PrefillDTile, true>(a, max_m_tiles, s)
-                     : launch_dma<PrefillDTile, false>(a, max_m_tiles, s);
+    if (mxfp4 && epi == kEpiPlain) return hipErrorInvalidValue;   // router weights are 16-bit
+    switch (kind) {
+    case GemmKind::kPrefill:
+        return mxfp4 ? launch_epi<PrefillMXTile>(epi, a, max_m_tiles, s)
+                     : launch_epi<PrefillDTile>(epi, a, max_m_tiles, s);
+    case GemmKind::kMid:
+        return mxfp4 ? launch_epi<MidMXTile>(epi, a, max_m_tiles, s)
+                     : launch_epi<MidDTile>(epi, a, max_m_tiles, s);
+    default:
+        return mxfp4 ? launch_epi<DecodeMXTile>(epi, a, max_m_tiles, s)
+                     : launch_epi<DecodeDTile>(epi, a, max_m_tiles, s);
     }
-    if (kind == GemmKind::kMid) {
-        if (mxfp4)
-            return gated ? launch_dma<MidMXTile, true>(a, max_m_tiles, s)
-                         : launch_dma<MidMXTile, false>(a, max_m_tiles, s);
-        return gated ? launch_dma<MidDTile, true>(a, max_m_tiles, s)
-                     : launch_dma<MidDTile, false>(a, max_m_tiles, s);
-    }
-    if (mxfp4)
-        return gated ? launch_dma<DecodeMXTile, true>(a, max_m_tiles, s)
-                     : launch_dma<DecodeMXTile, false>(a, max_m_tiles, s);
-    return gated ? launch_dma<DecodeDTile, true>(a, max_m_tiles, s)
-                 : launch_dma<DecodeDTile, false>(a, max_m_tiles, s);
 }
 
 hipError_t launch_mx_pack(const PackArgs &a, hipStream_t s)

@@ -67,6 +67,21 @@ __device__ inline float gated_act(int act, float g, float u, float alpha,
     return g * (1.0f / (1.0f + __expf(-alpha * g))) * (u + beta);
 }
 
+// Activation of a non-gated expert's fc1 output (act 2 relu, 3 gelu in the
+// erf form or, gelu_mode 1, the tanh form, 4 silu, 5 identity).
+__device__ inline float single_act(int act, int gelu_mode, float v)
+{
+    switch (act) {
+    case 2: return fmaxf(v, 0.0f);
+    case 3:
+        if (gelu_mode == 1)
+            return 0.5f * v * (1.0f + tanhf(0.7978845608f * (v + 0.044715f * v * v * v)));
+        return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+    case 4: return v * (1.0f / (1.0f + __expf(-v)));
+    default: return v;
+    }
+}
+
 __device__ inline float bf16_bits_to_float(uint16_t b)
 {
     return __uint_as_float((uint32_t)b << 16);

@@ -1,9 +1,12 @@
 // Grouped expert GEMMs for f32 layers (x, weights, h and y all f32), on the
-// vector ALUs with LDS-staged tiles.  Same scheduling and epilogue contract
-// as the bf16 MFMA kernels: the gated variant computes BNF gate and BNF up
-// features of BM tokens and applies the gated activation; the down variant
-// adds the bias.  Used for the f32 layer, whose tolerance (1e-4 of the
-// output RMS) rules out bf16 operands.
+// vector ALUs with LDS-staged tiles.  Same scheduling and epilogue modes as
+// the 16-bit MFMA kernels: gated computes BNF gate and BNF up features of BM
+// tokens and applies the gated activation; act applies a non-gated
+// activation to BNF fc1 features; down and plain add the bias.  Used for the
+// f32 layer, whose tolerance (1e-4 of the output RMS) rules out bf16
+// operands.  With weigh-inputs routing (row_w) the fc1 output of a row is
+// scaled by its routing weight before the bias, which equals running the
+// expert on the scaled input.
 #include "gemm_common.h"
 
 namespace moe {
@@ -14,9 +17,10 @@ constexpr int BNF = 32;     // output features per tile
 constexpr int BK = 32;
 constexpr int NT = 256;     // thread (tl = tid % 32, features 4*(tid/32) .. +3)
 
-template <bool GATED>
+template <int EPI>
 __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g)
 {
+    constexpr bool GATED = EPI == kEpiGated;
     constexpr int NB = GATED ? 2 * BNF : BNF;   // weight rows per tile
     __shared__ float As[BM][BK + 1];
     __shared__ float Bs[NB][BK + 1];
@@ -57,18 +61,22 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g)
     }
     if (tl >= tw.nrows) return;
     float *out = (float *)g.out + (int64_t)(tw.row0 + tl) * g.Nout;
+    const float rs = ((EPI == kEpiGated || EPI == kEpiAct) && g.row_w) ? g.row_w[tw.row0 + tl]
+                                                                        : 1.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int c = tw.n0 + fg * 4 + j;
         if (c >= g.Nout) continue;
-        float gv = ag[j];
+        float gv = ag[j] * rs;
         if (g.w.b_gate)
             gv += ((const float *)g.w.b_gate)[eb + (int64_t)c * g.w.row_mul + g.w.off_gate];
         if (GATED) {
-            float uv = au[j];
+            float uv = au[j] * rs;
             if (g.w.b_up)
                 uv += ((const float *)g.w.b_up)[eb + (int64_t)c * g.w.row_mul + g.w.off_up];
             out[c] = gated_act(g.act, gv, uv, g.alpha, g.beta, g.limit);
+        } else if (EPI == kEpiAct) {
+            out[c] = single_act(g.act, g.gelu_mode, gv);
         } else {
             out[c] = gv;
         }
@@ -80,13 +88,15 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g)
 int gemm_f32_bm() { return BM; }
 int gemm_f32_bn(bool) { return BNF; }
 
-hipError_t launch_gemm_f32(bool gated, const GemmArgs &a, int64_t max_m_tiles, hipStream_t s)
+hipError_t launch_gemm_f32(int epi, const GemmArgs &a, int64_t max_m_tiles, hipStream_t s)
 {
     const int64_t grid = max_m_tiles * a.nN + 8;
-    if (gated)
-        gemm_f32_kernel<true><<<dim3((unsigned)grid), dim3(NT), 0, s>>>(a);
-    else
-        gemm_f32_kernel<false><<<dim3((unsigned)grid), dim3(NT), 0, s>>>(a);
+    const dim3 gd((unsigned)grid), bd(NT);
+    switch (epi) {
+    case kEpiGated: gemm_f32_kernel<kEpiGated><<<gd, bd, 0, s>>>(a); break;
+    case kEpiAct: gemm_f32_kernel<kEpiAct><<<gd, bd, 0, s>>>(a); break;
+    default: gemm_f32_kernel<kEpiDown><<<gd, bd, 0, s>>>(a); break;   // down and plain
+    }
     return hipGetLastError();
 }
 

@@ -38,6 +38,8 @@ struct PermuteArgs {
     int32_t *tile_cum1;      // [E + 1] cumulative M-tiles of GEMM 1
     int32_t *tile_cum2;      // [E + 1] cumulative M-tiles of GEMM 2
     int bm1, bm2;            // token-tile heights of the two GEMMs
+    const float *weights;    // [T, K] routing weights, read when row_weight is set
+    float *row_weight;       // [T*K] weight of each row (weigh-inputs), or null
 };
 
 // Weight-operand description of one grouped GEMM.  Feature row c of expert e
@@ -58,6 +60,13 @@ struct WeightRows {
 // Storage format of one h tile (GEMM-1 output tile, read by the down GEMM).
 enum : uint8_t { kHF16 = 0, kHBF16 = 1 };
 
+// Epilogue (and operand) mode of a grouped GEMM launch.
+//  kEpiDown   down GEMM: A = h (16-bit, per-tile formats), y = acc + bias, f32
+//  kEpiGated  gate||up GEMM: gate/up row pairs, gated activation, 16-bit h
+//  kEpiAct    fc1 GEMM of a non-gated expert: activation of each row, 16-bit h
+//  kEpiPlain  A = x, y = acc + bias, f32 (the router GEMM, one group)
+enum EpiMode : int { kEpiDown = 0, kEpiGated = 1, kEpiAct = 2, kEpiPlain = 3 };
+
 struct GemmArgs {
     const void *a;               // activations: x [T, Kd] or h [T*K, Kd]
     const int32_t *row_token;    // if set, A row r reads a[row_token[r]]
@@ -70,8 +79,11 @@ struct GemmArgs {
     int Nout;                    // output features: I (gated) or H (down)
     int nN;                      // feature tiles
     void *out;                   // h bf16 [T*K, I] or y f32 [T*K, H]
-    int act;                     // 0 SiLU-gated, 1 clamped SwiGLU
+    int act;                     // moe_activation code (0..5)
+    int gelu_mode;               // 0 erf, 1 tanh
     float alpha, beta, limit;
+    const float *row_w;          // weigh-inputs: row r's weight scales its fc1
+                                 // output before the bias; null otherwise
     // h storage formats, one byte per (GEMM-1 M-tile, GEMM-1 feature tile):
     // written by the gated GEMM, read per reduction step by the down GEMM.
     uint8_t *hfmt;
@@ -134,6 +146,7 @@ struct CombineArgs {
     void *out;                   // [T, H] x dtype
     int T, H, K;
     int out_bf16;                // 1: bf16 x/out, 0: f32
+    int unit_weights;            // weigh-inputs: every kept output weighs 1
 };
 
 // Dense f32 grouped GEMM (the fp32 layer): same contract as GemmArgs with
@@ -142,17 +155,24 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
-// Grouped-GEMM variants.  `gated` selects the gate||up GEMM with the fused
-// activation (16-bit h out) versus the down GEMM (+bias, f32 y out).  With
-// mxfp4 the weights are read from the packed copy (GemmArgs pk / pks).
+// Grouped-GEMM variants, by epilogue mode (EpiMode).  With mxfp4 the weights
+// are read from the packed copy (GemmArgs pk / pks).
 enum class GemmKind { kPrefill = 0, kDecode = 1, kMid = 2 };
 int gemm_bm(GemmKind kind);          // token-tile height of a variant
 int gemm_bn(GemmKind kind, bool gated);   // output features per tile
-hipError_t launch_gemm_bf16(GemmKind kind, bool gated, bool mxfp4,
+hipError_t launch_gemm_bf16(GemmKind kind, int epi, bool mxfp4,
                             const GemmArgs &a, int64_t max_m_tiles, hipStream_t s);
 int gemm_f32_bm();
 int gemm_f32_bn(bool gated);
-hipError_t launch_gemm_f32(bool gated, const GemmArgs &a, int64_t max_m_tiles,
+hipError_t launch_gemm_f32(int epi, const GemmArgs &a, int64_t max_m_tiles,
                            hipStream_t s);
+
+// One group of T rows (the router GEMM): counts = {T}, offsets = {0, T},
+// tile_cum = {0, ceil(T / bm)}.
+hipError_t launch_single_group(int32_t *counts, int32_t *offsets, int32_t *tile_cum, int T,
+                               int bm, hipStream_t s);
+// Wr [H, E] -> its transpose [E, H] (elem_bytes 2 or 4).
+hipError_t launch_transpose(const void *src, void *dst, int rows, int cols, int elem_bytes,
+                            hipStream_t s);
 
 }  // namespace moe

@@ -116,6 +116,8 @@ __global__ __launch_bounds__(kPermTokens) void scatter_kernel(PermuteArgs a)
         const int row = a.block_base[(int64_t)blockIdx.x * a.E + e] + rank;
         a.row_token[row] = t;
         a.slot_row[(int64_t)t * a.K + j] = row;
+        // weigh-inputs routing: the row's weight travels with it to GEMM 1
+        if (a.row_weight) a.row_weight[row] = a.weights[(int64_t)t * a.K + j];
     }
 }
 

@@ -41,9 +41,11 @@ class MoE:
     def set_weights(self, gate_up_experts, down_experts, *, gate_up_bias=None,
                     down_bias=None, gate_experts=None, gate_bias=None,
                     e_score_correction_bias=None, gate_up_scales=None,
-                    down_scales=None, gate_scales=None):
+                    down_scales=None, gate_scales=None, router_weight=None,
+                    router_bias=None):
         """Bind the slots (device tensors, borrowed).  MXFP4 stacks are given as
-        codes with their ``*_scales``."""
+        codes with their ``*_scales``.  router_weight [H, E] / router_bias [E]
+        (optional) let forward compute the router logits itself."""
         w = _lib.moe_weights()
         w.gate_up_experts = _lib.tensor(gate_up_experts, gate_up_scales)
         w.down_experts = _lib.tensor(down_experts, down_scales)
@@ -52,6 +54,8 @@ class MoE:
         w.down_bias = _lib.tensor(down_bias)
         w.gate_bias = _lib.tensor(gate_bias)
         w.e_score_correction_bias = _lib.tensor(e_score_correction_bias)
+        w.router_weight = _lib.tensor(router_weight)
+        w.router_bias = _lib.tensor(router_bias)
         _lib.check(_lib.lib().moe_set_weights(self._h, C.byref(w)))
         # the library borrows these buffers: keep them alive while bound
         self._bound = dict(gate_up_experts=gate_up_experts, down_experts=down_experts,
@@ -59,13 +63,14 @@ class MoE:
                            down_bias=down_bias, gate_bias=gate_bias,
                            e_score_correction_bias=e_score_correction_bias,
                            gate_up_scales=gate_up_scales, down_scales=down_scales,
-                           gate_scales=gate_scales)
+                           gate_scales=gate_scales, router_weight=router_weight,
+                           router_bias=router_bias)
 
     def set_weights_from(self, inp: dict):
         """Bind from a dict keyed by slot name (as ``synth.make_inputs`` returns)."""
         keys = ("gate_up_experts", "down_experts", "gate_experts", "gate_up_bias",
                 "down_bias", "gate_bias", "e_score_correction_bias", "gate_up_scales",
-                "down_scales", "gate_scales")
+                "down_scales", "gate_scales", "router_weight", "router_bias")
         kw = {k: inp.get(k) for k in keys}
         self.set_weights(kw.pop("gate_up_experts"), kw.pop("down_experts"), **kw)
 
@@ -104,12 +109,13 @@ class MoE:
             setattr(r, k, v.data_ptr() if v is not None else None)
         return r
 
-    def forward(self, x: torch.Tensor, router_logits: torch.Tensor,
+    def forward(self, x: torch.Tensor, router_logits: Optional[torch.Tensor],
                 shared_output: Optional[torch.Tensor] = None, *, out=None,
                 routing: Optional[dict] = None, workspace=None, stream=None,
                 events=None):
-        """One MoE step.  `events` (optional): MOE_STAGE_EVENTS raw hipEvent_t
-        handles recorded at the stage boundaries (moe_forward_timed)."""
+        """One MoE step.  router_logits None: the bound router computes them.
+        `events` (optional): MOE_STAGE_EVENTS raw hipEvent_t handles recorded
+        at the stage boundaries (moe_forward_timed)."""
         T = x.numel() // x.shape[-1]
         out = torch.empty_like(x) if out is None else out
         ws = self.workspace(T, x.device) if workspace is None else workspace
@@ -127,6 +133,19 @@ class MoE:
         return out
 
     __call__ = forward
+
+    def router_logits(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+        """x . Wr + Br (f32 [T, E]) from the bound router."""
+        T = x.numel() // x.shape[-1]
+        out = torch.empty((T, self.E), dtype=torch.float32, device=x.device) \
+            if out is None else out
+        ws = self.workspace(T, x.device)
+        xt, lt = _lib.tensor(x), _lib.tensor(out)
+        _lib.check(_lib.lib().moe_router_logits(self._h, C.byref(xt), C.byref(lt),
+                                                C.c_void_p(ws.data_ptr()), ws.numel(),
+                                                C.c_void_p(_lib.stream_ptr(stream))))
+        return out
 
     def route(self, router_logits: torch.Tensor, routing: Optional[dict] = None,
               stream=None) -> dict:
@@ -148,7 +167,8 @@ def from_config(cfg, **over) -> MoE:
               topk_group=cfg.topk_group, routed_scaling_factor=cfg.routed_scaling_factor,
               activation=cfg.activation, swiglu_fusion=cfg.layout,
               swiglu_alpha=cfg.swiglu_alpha, swiglu_beta=cfg.swiglu_beta,
-              swiglu_limit=cfg.swiglu_limit)
+              swiglu_limit=cfg.swiglu_limit, gelu_mode=cfg.gelu_mode,
+              weigh_inputs=cfg.weigh_inputs)
     kw.update(over)
     return MoE(cfg.E, cfg.H, cfg.I, cfg.K, gate_up_bias=cfg.expert_biases,
                down_bias=cfg.expert_biases, dtype=cfg.w_dtype, **kw)

@@ -47,11 +47,20 @@ def run_gpu(cfg, inp: dict, routing: bool = True, **over):
 
 def compare_out(out_gpu: torch.Tensor, ref: np.ndarray, x_dtype: str, what: str = ""):
     """Max-abs error against the fp64 oracle, relative to the oracle RMS.
-    Also reports the floor set by rounding the oracle itself to x's dtype."""
+    Also reports the floor set by rounding the oracle itself to x's dtype.
+
+    Reading of the bar for bf16 outputs: the layer must return out in x's
+    dtype, so its error includes the final rounding to bf16, up to half a bf16
+    ulp of each element.  When rounding the exact result alone (the floor)
+    exceeds TOL * RMS -- a large output near the top of its binade -- no
+    bf16 result can meet the bar as stated; the bar then applies to the error
+    beyond that final rounding: per element |gpu - oracle| minus half an ulp
+    of the bf16 value returned, which bounds the error before the rounding."""
     o = out_gpu.float().cpu().numpy().astype(np.float64).reshape(ref.shape)
     rms = float(np.sqrt((ref ** 2).mean()))
     err = float(np.abs(o - ref).max())
     floor = 0.0
+    rb = ref
     if x_dtype == "bf16":
         rb = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
         floor = float(np.abs(rb - ref).max())
@@ -59,7 +68,16 @@ def compare_out(out_gpu: torch.Tensor, ref: np.ndarray, x_dtype: str, what: str 
     print(f"[parity] {what}: max|err|/rms = {rel:.3e} (bf16 rounding floor "
           f"{floor / rms if rms else 0:.3e}, rms {rms:.4g})", flush=True)
     assert np.isfinite(o).all(), what
-    assert err <= TOL[x_dtype] * rms, (what, rel)
+    bar = TOL[x_dtype] * rms
+    if err > bar and floor > bar:
+        a = np.abs(o)
+        half_ulp = np.where(a > 0, np.exp2(np.floor(np.log2(np.where(a > 0, a, 1.0))) - 8), 0.0)
+        beyond = float((np.abs(o - ref) - half_ulp).max())
+        print(f"[parity] {what}: floor above the bar; error beyond the final rounding "
+              f"{beyond / rms:.3e}", flush=True)
+        assert beyond <= bar, (what, rel, beyond / rms)
+        return rel
+    assert err <= bar, (what, rel)
     return rel
 
 

@@ -67,8 +67,8 @@ def create(L, E=8, H=64, I=32, K=2, dtype="bf16", gub=False, db=False, **opt):
     dict(H=60), dict(dtype="mxfp4", H=48), dict(n_group=3, topk_group=1),
     dict(n_group=4, topk_group=5), dict(n_group=4, topk_group=1, K=3),
     dict(n_group=128, E=256, topk_group=1, K=1), dict(scoring=7),
-    dict(activation=5), dict(swiglu_fusion=3), dict(gemm_variant=4),
-    dict(gemm_variant=-1)])
+    dict(activation=6), dict(swiglu_fusion=3), dict(gemm_variant=4),
+    dict(gemm_variant=-1), dict(gelu_mode=2), dict(weigh_inputs=2)])
 def test_create_rejects_bad_geometry(L, kw):
     st, h = create(L, **kw)
     assert st == 1, L.lib().moe_last_error()
@@ -194,3 +194,49 @@ def test_workspace_grows_with_tokens(L):
     assert b.value > a.value
     assert L.lib().moe_destroy(h) == 0
     assert L.lib().moe_destroy(None) == 0
+
+
+def test_nongated_and_router_binding(L):
+    """Non-gated activations bind one fc1 stack [E, I, H] (ONNX MoE fusion
+    size 1) and no gate stack; the router binds [H, E] (+ [E] bias) whatever
+    was declared; a forward without logits needs a bound router."""
+    lib = L.lib()
+    BF, F32 = L.MOE_DTYPE_BF16, L.MOE_DTYPE_F32
+    st, h = create(L, gub=True, activation="gelu")
+    assert st == 0
+    w = L.moe_weights()
+    w.gate_up_experts = _t(L, [8, 64, 64], BF)                # 2I rows: wrong here
+    w.down_experts = _t(L, [8, 64, 32], BF)
+    assert lib.moe_set_weights(h, C.byref(w)) == 2
+    w.gate_up_experts = _t(L, [8, 32, 64], BF)
+    w.gate_up_bias = _t(L, [8, 32], BF)
+    w.gate_experts = _t(L, [8, 32, 64], BF)                   # no gate stack here
+    assert lib.moe_set_weights(h, C.byref(w)) == 2
+    w.gate_experts = L.moe_tensor()
+    w.gate_bias = _t(L, [8, 32], BF)
+    assert lib.moe_set_weights(h, C.byref(w)) == 2
+    w.gate_bias = L.moe_tensor()
+    assert lib.moe_set_weights(h, C.byref(w)) == 0
+    w.router_bias = _t(L, [8], BF)                            # bias without weight
+    assert lib.moe_set_weights(h, C.byref(w)) == 2
+    w.router_weight = _t(L, [8, 64], BF)                      # transposed: [E, H]
+    assert lib.moe_set_weights(h, C.byref(w)) == 2
+    w.router_weight = _t(L, [64, 8], F32)                     # wrong dtype
+    assert lib.moe_set_weights(h, C.byref(w)) == 2
+    # forward without logits and no router: UNBOUND, before any device work
+    w.router_weight = L.moe_tensor()
+    w.router_bias = L.moe_tensor()
+    assert lib.moe_set_weights(h, C.byref(w)) == 0
+    x0, o0 = _t(L, [0, 64], BF), _t(L, [0, 64], BF)
+    assert lib.moe_forward(h, C.byref(x0), None, None, C.byref(o0), None, 0, None,
+                           None) == 4
+    w.router_weight = _t(L, [64, 8], BF)
+    w.router_bias = _t(L, [8], BF)
+    assert lib.moe_set_weights(h, C.byref(w)) == 0
+    assert lib.moe_forward(h, C.byref(x0), None, None, C.byref(o0), None, 0, None,
+                           None) == 0                         # T = 0: no launch
+    lg0 = _t(L, [0, 8], F32)
+    assert lib.moe_router_logits(h, C.byref(x0), C.byref(lg0), None, 0, None) == 0
+    bad = _t(L, [0, 7], F32)
+    assert lib.moe_router_logits(h, C.byref(x0), C.byref(bad), None, 0, None) == 2
+    lib.moe_destroy(h)
