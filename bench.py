@@ -97,18 +97,19 @@ def cpu_baseline(cfg, inp, budget_s: float, stream_bytes=None):
     p = oracle.params_of(cfg)
     rng = np.random.default_rng(1)
     t0 = time.perf_counter()
-    oracle.forward(p, host, tokens=np.arange(min(threads, cfg.T)), threads=threads)
+    oracle.forward(p, host, tokens=np.arange(min(threads, cfg.T)), threads=threads,
+                   use_router=cfg.router)
     per_tok = (time.perf_counter() - t0) / min(threads, cfg.T)
     n = int(max(threads, min(cfg.T, budget_s / max(per_tok, 1e-6))))
     n = (n // threads) * threads or threads
     toks = np.sort(rng.choice(cfg.T, size=min(n, cfg.T), replace=False))
     t0 = time.perf_counter()
-    oracle.forward(p, host, tokens=toks, threads=threads)
+    oracle.forward(p, host, tokens=toks, threads=threads, use_router=cfg.router)
     dt = time.perf_counter() - t0
     if stream_bytes is not None and len(toks) == cfg.T:
         value, unit = stream_bytes / dt / 1e9, "GB/s"
     else:
-        value, unit = 6.0 * cfg.K * cfg.H * cfg.I * len(toks) / dt / 1e12, "TFLOP/s"
+        value, unit = cfg.flops / cfg.T * len(toks) / dt / 1e12, "TFLOP/s"
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"{len(toks)} of {cfg.T} tokens of {cfg.name} (full weights), "
                       f"{dt:.3g} s on {threads} threads; {len(toks) / dt:.2f} tokens/s"}
@@ -122,6 +123,12 @@ def main():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--activation", default=None,
+                    help="override the workload's activation (e.g. relu, gelu, identity)")
+    ap.add_argument("--weigh-inputs", action="store_true",
+                    help="weigh-inputs routing (weights scale the experts' inputs)")
+    ap.add_argument("--router", action="store_true",
+                    help="the layer's own router computes the logits (x.Wr+Br) in the step")
     ap.add_argument("--gemm-variant", type=int, default=0,
                     help="grouped-GEMM tiles: 0 auto, 1 256-row, 2 32-row, 3 128-row")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -137,6 +144,15 @@ def main():
     from mixture_experts_ffn_03_amd import from_config, synth
 
     cfg = synth.CONFIGS[args.workload]
+    over = {}
+    if args.activation:
+        over["activation"] = args.activation
+    if args.weigh_inputs:
+        over["weigh_inputs"] = True
+    if args.router:
+        over["router"] = True
+    if over:
+        cfg = cfg.replace(**over)
     dev = torch.device("cuda:0")
     log(f"[bench] generating {cfg.name} inputs on {dev}")
     inp = synth.make_inputs(cfg, device=dev)
@@ -145,10 +161,14 @@ def main():
     x, lg = inp["x"], inp["logits"]
     out = torch.empty_like(x)
     ws = layer.workspace(cfg.T, dev)
+    # with the layer's own router the step computes the logits itself
+    step_logits = None if cfg.router else lg
+    if cfg.router:
+        lg = layer.router_logits(x)
     # experts that receive tokens (their weights are the ones a step streams)
     touched = int((layer.route(lg)["expert_counts"] > 0).sum().item())
     wb = 0.5 + 1.0 / 32.0 if cfg.w_dtype == "mxfp4" else (4.0 if cfg.w_dtype == "f32" else 2.0)
-    gu_bytes = 2.0 * cfg.I * cfg.H * wb
+    gu_bytes = (2.0 if cfg.gated else 1.0) * cfg.I * cfg.H * wb
     dn_bytes = 1.0 * cfg.H * cfg.I * wb
     # few rows per expert: the step streams weights (same threshold the library
     # uses to pick its small-M tiles)
@@ -166,14 +186,14 @@ def main():
     evs = [[hip.event() for _ in range(6)] for _ in range(args.steps)]
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
-        layer(x, lg, out=out, workspace=ws)
+        layer(x, step_logits, out=out, workspace=ws)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} steps")
     start.record()
     for k in range(args.steps):
-        layer(x, lg, out=out, workspace=ws, events=evs[k])
+        layer(x, step_logits, out=out, workspace=ws, events=evs[k])
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -187,7 +207,7 @@ def main():
             hip.destroy(e)
 
     flops = float(cfg.flops)
-    gemm1_flops = 4.0 * cfg.T * cfg.K * cfg.H * cfg.I
+    gemm1_flops = (4.0 if cfg.gated else 2.0) * cfg.T * cfg.K * cfg.H * cfg.I
     g1 = stage_ms["gemm_gate_up"]
     traffic = load_traffic(cfg.name)
     if decode:
@@ -221,7 +241,9 @@ def main():
         "data": "synthetic (seeded, random-init weights of the workload's shape)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
                    "K": cfg.K, "layout": cfg.layout, "weights": cfg.w_dtype,
-                   "scoring": cfg.scoring, "parallelism": "none (1 GPU)"},
+                   "scoring": cfg.scoring, "activation": cfg.activation,
+                   "weigh_inputs": cfg.weigh_inputs, "router_in_step": cfg.router,
+                   "parallelism": "none (1 GPU)"},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "active_tflops": flops / (ms * 1e-3) / 1e12,
         "weight_stream_gbs": touched * (gu_bytes + dn_bytes) / (ms * 1e-3) / 1e9,

@@ -318,7 +318,10 @@ moe_status run_router(const moe_layer *l, const void *x, int64_t T, float *logit
     g.E = 1;
     g.Kd = (int)l->H;
     g.Nout = (int)l->E;
-    const int bm = path_bm(path), bn = path_bn(path, false);
+    // one group of T rows and few (E) features: the 32-row tiles give T / 32
+    // workgroups where 256-row tiles would leave most CUs idle
+    const Path rp = path == Path::kF32 ? Path::kF32 : Path::kDecode;
+    const int bm = path_bm(rp), bn = path_bn(rp, false);
     g.nN = (int)((l->E + bn - 1) / bn);
     g.out = logits;
     g.w.w_gate = g.w.w_up = l->wr_t;
@@ -329,9 +332,9 @@ moe_status run_router(const moe_layer *l, const void *x, int64_t T, float *logit
                               "router setup launch");
     if (st) return st;
     const int64_t m_tiles = (T + bm - 1) / bm;
-    if (path == Path::kF32)
+    if (rp == Path::kF32)
         return hip_check(launch_gemm_f32(kEpiPlain, g, m_tiles, s), "router launch");
-    return hip_check(launch_gemm_bf16(kind_of(path), kEpiPlain, false, g, m_tiles, s),
+    return hip_check(launch_gemm_bf16(kind_of(rp), kEpiPlain, false, g, m_tiles, s),
                      "router launch");
 }
 

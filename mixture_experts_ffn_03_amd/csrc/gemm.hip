@@ -660,7 +660,10 @@ hipError_t launch_epi(int epi, const GemmArgs &a, int64_t max_m_tiles, hipStream
     switch (epi) {
     case kEpiGated: return launch_dma<TL, kEpiGated>(a, max_m_tiles, s);
     case kEpiAct: return launch_dma<TL, kEpiAct>(a, max_m_tiles, s);
-    case kEpiPlain: return launch_dma<TL, kEpiPlain>(a, max_m_tiles, s);
+    case kEpiPlain:
+        // the router GEMM runs on the 16-bit 32-row tiles only
+        if constexpr (!TL::MX && TL::BM == 32) return launch_dma<TL, kEpiPlain>(a, max_m_tiles, s);
+        else return hipErrorInvalidValue;
     default: return launch_dma<TL, kEpiDown>(a, max_m_tiles, s);
     }
 }
