@@ -147,6 +147,7 @@ size_t align256(size_t v)
 // Workspace carving.  Every region starts on a 256-byte boundary.
 struct Workspace {
     size_t ids, weights, block_counts, block_base, counts, offsets, tile_cum1, tile_cum2,
+        full_cum1, full_cum2,
         row_token, slot_row, row_weight, logits, router_grp, hfmt, h, y, total;
 };
 
@@ -176,11 +177,13 @@ Workspace layout(const moe_layer *l, int64_t T)
     w.offsets = take((l->E + 1) * 4);
     w.tile_cum1 = take((l->E + 1) * 4);
     w.tile_cum2 = take((l->E + 1) * 4);
+    w.full_cum1 = take((l->E + 1) * 4);
+    w.full_cum2 = take((l->E + 1) * 4);
     w.row_token = take(TK * 4);
     w.slot_row = take(TK * 4);
     w.row_weight = take(TK * 4);          // weigh-inputs: routing weight per row
     w.logits = take(T * l->E * 4);        // router logits when the layer's router runs
-    w.router_grp = take(8 * 4);           // router GEMM: counts, offsets, tile_cum
+    w.router_grp = take(8 * 4);   // router GEMM: counts, offsets, tile_cum, full_cum
     // one h-format byte per (GEMM-1 M-tile, GEMM-1 feature tile), worst case
     // over the two 16-bit kernel variants
     size_t nfmt = 0;
@@ -292,6 +295,8 @@ moe_status run_route(const moe_layer *l, const float *logits, int64_t T, char *w
     pa.slot_row = (int32_t *)(ws + W.slot_row);
     pa.tile_cum1 = (int32_t *)(ws + W.tile_cum1);
     pa.tile_cum2 = (int32_t *)(ws + W.tile_cum2);
+    pa.full_cum1 = (int32_t *)(ws + W.full_cum1);
+    pa.full_cum2 = (int32_t *)(ws + W.full_cum2);
     pa.bm1 = path_bm(path);
     pa.bm2 = path_bm(path);
     pa.weights = ra.weights;
@@ -315,6 +320,7 @@ moe_status run_router(const moe_layer *l, const void *x, int64_t T, float *logit
     g.counts = grp;
     g.offsets = grp + 1;
     g.tile_cum = grp + 3;
+    g.full_cum = grp + 5;
     g.E = 1;
     g.Kd = (int)l->H;
     g.Nout = (int)l->E;
@@ -328,7 +334,7 @@ moe_status run_router(const moe_layer *l, const void *x, int64_t T, float *logit
     g.w.e_rows = l->E;
     g.w.row_mul = 1;
     if (present(l->w.router_bias)) g.w.b_gate = l->w.router_bias.data;
-    moe_status st = hip_check(launch_single_group(grp, grp + 1, grp + 3, (int)T, bm, s),
+    moe_status st = hip_check(launch_single_group(grp, grp + 1, grp + 3, grp + 5, (int)T, bm, s),
                               "router setup launch");
     if (st) return st;
     const int64_t m_tiles = (T + bm - 1) / bm;
@@ -764,6 +770,7 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     g1.counts = (const int32_t *)(wsb + W.counts);
     g1.offsets = (const int32_t *)(wsb + W.offsets);
     g1.tile_cum = (const int32_t *)(wsb + W.tile_cum1);
+    g1.full_cum = (const int32_t *)(wsb + W.full_cum1);
     g1.E = (int)l->E;
     g1.Kd = (int)l->H;
     g1.Nout = (int)l->I;
@@ -824,6 +831,7 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     g2.counts = g1.counts;
     g2.offsets = g1.offsets;
     g2.tile_cum = (const int32_t *)(wsb + W.tile_cum2);
+    g2.full_cum = (const int32_t *)(wsb + W.full_cum2);
     g2.E = (int)l->E;
     g2.Kd = (int)l->I;
     g2.Nout = (int)l->H;

@@ -292,8 +292,8 @@ struct DTile {
     static_assert(2 * NB <= 63, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     static_assert(B_BYTES % 1024 == 0 || MX, "KiB-aligned stages");
-    static_assert(LDS_BYTES >= (kMaxExperts + 1) * 4 && LDS_BYTES >= NWAVES * 4,
-                  "scheduling table and epilogue scratch overlay the stages");
+    static_assert(LDS_BYTES >= 2 * (kMaxExperts + 1) * 4 && LDS_BYTES >= NWAVES * 4,
+                  "scheduling tables and epilogue scratch overlay the stages");
     // swizzle of token row r: rows r and r + 16/CPR start in the same bank group
     __device__ static inline int sw(int r) { return (r / (16 / CPR)) % CPR; }
     static_assert(CPR == 4 || CPR == 8 || CPR == 16, "row of 64, 128 or 256 bytes");

@@ -16,34 +16,67 @@ struct TileWork {
 
 // Map this workgroup to a tile, or return false when it has none.
 //
-// Tiles are numbered expert-major, then feature tile, then token tile, so
-// the token tiles that share one expert's weight panel are consecutive.
-// Hardware dispatches workgroup b to XCD b % 8; consecutive tile numbers are
-// gathered onto one XCD (its L2 then serves the shared weight panel and the
-// shared activation rows), with the XCD loads differing by at most one tile.
-// The count of tiles is data dependent and read from tile_cum (staged in
-// LDS); surplus workgroups of the worst-case grid return at once.
+// Two classes of tiles: full ones (bm rows) and each expert's last, partial
+// one.  Full tiles all take the same time, so the workgroups that share a
+// weight panel or a token block run side by side and the XCD's L2 serves
+// the repeats of each k-slice; a partial tile skips its empty row blocks and
+// finishes early, and interleaved with full tiles it would let its CU run
+// ahead and scatter the sharers apart in time (measured: about twice the
+// memory traffic).  So every full tile comes first, the partial ones last.
+// Within each class tiles are numbered expert-major, then feature tile, then
+// token tile, so the token tiles that share one expert's weight panel are
+// consecutive.  Hardware dispatches workgroup b to XCD b % 8; each class is
+// cut into 8 contiguous chunks, one per XCD (its L2 then serves the shared
+// panels and rows), and workgroup slot b / 8 walks its XCD's full chunk and
+// then its partial chunk.  The count of tiles is data dependent: the
+// prefix sums are staged in LDS, and surplus workgroups of the worst-case
+// grid return at once.
 __device__ inline bool find_tile(const GemmArgs &g, int *s_cum, int bm, int n_width,
                                  TileWork *w)
 {
-    for (int i = threadIdx.x; i <= g.E; i += blockDim.x) s_cum[i] = g.tile_cum[i];
-    __syncthreads();
-    const int total = s_cum[g.E] * g.nN;
-    const int bid = blockIdx.x;
-    const int q = total >> 3, rem = total & 7, xcd = bid & 7, slot = bid >> 3;
-    if (slot >= q + (xcd < rem ? 1 : 0)) return false;
-    const int v = xcd * q + min(xcd, rem) + slot;
-    // expert e with s_cum[e]*nN <= v < s_cum[e+1]*nN (it has >= 1 tile)
-    int lo = 0, hi = g.E;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_cum[mid] * g.nN <= v) lo = mid;
-        else hi = mid;
+    int *s_full = s_cum + g.E + 1;
+    for (int i = threadIdx.x; i <= g.E; i += blockDim.x) {
+        s_cum[i] = g.tile_cum[i];
+        s_full[i] = g.full_cum[i];
     }
-    const int e = lo;
-    const int mt = s_cum[e + 1] - s_cum[e];
-    const int local = v - s_cum[e] * g.nN;
-    const int nt = local / mt, mtile = local - nt * mt;
+    __syncthreads();
+    const int nN = g.nN;
+    const int F = s_full[g.E] * nN;               // full tiles
+    const int P = s_cum[g.E] * nN - F;            // partial tiles (one per expert and N tile)
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int qF = F >> 3, rF = F & 7, qP = P >> 3, rP = P & 7;
+    const int cntF = qF + (xcd < rF ? 1 : 0);
+    const int cntP = qP + (xcd < rP ? 1 : 0);
+    int e, nt, mtile;
+    if (slot < cntF) {
+        const int v = xcd * qF + min(xcd, rF) + slot;
+        // expert e with s_full[e]*nN <= v < s_full[e+1]*nN
+        int lo = 0, hi = g.E;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_full[mid] * nN <= v) lo = mid;
+            else hi = mid;
+        }
+        e = lo;
+        const int mt = s_full[e + 1] - s_full[e];
+        const int local = v - s_full[e] * nN;
+        nt = local / mt;
+        mtile = local - nt * mt;
+    } else if (slot < cntF + cntP) {
+        const int v = xcd * qP + min(xcd, rP) + (slot - cntF);
+        // partial tiles before expert e: (s_cum[e] - s_full[e]) * nN
+        int lo = 0, hi = g.E;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if ((s_cum[mid] - s_full[mid]) * nN <= v) lo = mid;
+            else hi = mid;
+        }
+        e = lo;
+        nt = v - (s_cum[e] - s_full[e]) * nN;
+        mtile = s_full[e + 1] - s_full[e];        // the last M-tile of expert e
+    } else {
+        return false;
+    }
     w->e = e;
     w->row0 = g.offsets[e] + mtile * bm;
     w->nrows = min(bm, g.counts[e] - mtile * bm);

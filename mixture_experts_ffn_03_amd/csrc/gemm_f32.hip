@@ -24,7 +24,7 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g)
     constexpr int NB = GATED ? 2 * BNF : BNF;   // weight rows per tile
     __shared__ float As[BM][BK + 1];
     __shared__ float Bs[NB][BK + 1];
-    __shared__ int s_cum[kMaxExperts + 1];
+    __shared__ int s_cum[2 * (kMaxExperts + 1)];
     TileWork tw;
     if (!find_tile(g, s_cum, BM, BNF, &tw)) return;
     const int tid = threadIdx.x, Kd = g.Kd;

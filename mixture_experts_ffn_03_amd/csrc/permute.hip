@@ -83,20 +83,28 @@ __global__ __launch_bounds__(1024) void scan_kernel(PermuteArgs a)
     const int off = block_exclusive_scan(e < a.E ? run : 0, buf, &total);
     const int mt1 = e < a.E ? (run + a.bm1 - 1) / a.bm1 : 0;
     const int mt2 = e < a.E ? (run + a.bm2 - 1) / a.bm2 : 0;
-    int tot1, tot2;
+    const int ft1 = e < a.E ? run / a.bm1 : 0;     // full M-tiles
+    const int ft2 = e < a.E ? run / a.bm2 : 0;
+    int tot1, tot2, ftot1, ftot2;
     const int cum1 = block_exclusive_scan(mt1, buf, &tot1);
     const int cum2 = block_exclusive_scan(mt2, buf, &tot2);
+    const int fcum1 = block_exclusive_scan(ft1, buf, &ftot1);
+    const int fcum2 = block_exclusive_scan(ft2, buf, &ftot2);
     if (e < a.E) {
         a.counts[e] = run;
         a.offsets[e] = off;
         a.tile_cum1[e] = cum1;
         a.tile_cum2[e] = cum2;
+        a.full_cum1[e] = fcum1;
+        a.full_cum2[e] = fcum2;
         for (int b = 0; b < NB; ++b) a.block_base[(int64_t)b * a.E + e] += off;
     }
     if (e == 0) {
         a.offsets[a.E] = total;
         a.tile_cum1[a.E] = tot1;
         a.tile_cum2[a.E] = tot2;
+        a.full_cum1[a.E] = ftot1;
+        a.full_cum2[a.E] = ftot2;
     }
 }
 

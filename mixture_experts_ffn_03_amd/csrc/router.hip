@@ -27,8 +27,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *src, T *dst, in
     }
 }
 
-__global__ void single_group_kernel(int32_t *counts, int32_t *offsets, int32_t *tile_cum, int T,
-                                    int bm)
+__global__ void single_group_kernel(int32_t *counts, int32_t *offsets, int32_t *tile_cum,
+                                    int32_t *full_cum, int T, int bm)
 {
     if (threadIdx.x == 0) {
         counts[0] = T;
@@ -36,6 +36,8 @@ __global__ void single_group_kernel(int32_t *counts, int32_t *offsets, int32_t *
         offsets[1] = T;
         tile_cum[0] = 0;
         tile_cum[1] = (T + bm - 1) / bm;
+        full_cum[0] = 0;
+        full_cum[1] = T / bm;
     }
 }
 
@@ -54,10 +56,10 @@ hipError_t launch_transpose(const void *src, void *dst, int rows, int cols, int 
     return hipGetLastError();
 }
 
-hipError_t launch_single_group(int32_t *counts, int32_t *offsets, int32_t *tile_cum, int T,
-                               int bm, hipStream_t s)
+hipError_t launch_single_group(int32_t *counts, int32_t *offsets, int32_t *tile_cum,
+                               int32_t *full_cum, int T, int bm, hipStream_t s)
 {
-    single_group_kernel<<<1, 64, 0, s>>>(counts, offsets, tile_cum, T, bm);
+    single_group_kernel<<<1, 64, 0, s>>>(counts, offsets, tile_cum, full_cum, T, bm);
     return hipGetLastError();
 }
 
