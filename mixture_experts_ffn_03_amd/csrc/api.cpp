@@ -157,47 +157,6 @@ int64_t max_m_tiles_of(const moe_layer *l, int64_t T, int bm)
     return (TK + bm - 1) / bm + (l->E < TK ? l->E : TK);
 }
 
-Workspace layout(const moe_layer *l, int64_t T)
-{
-    Workspace w{};
-    const int64_t TK = T * l->K;
-    const int64_t NB = (T + kPermTokens - 1) / kPermTokens;
-    const size_t hbytes = l->wdtype == MOE_DTYPE_F32 ? 4 : 2;
-    size_t o = 0;
-    auto take = [&](size_t bytes) {
-        size_t at = o;
-        o = align256(o + bytes);
-        return at;
-    };
-    w.ids = take(TK * 4);
-    w.weights = take(TK * 4);
-    w.block_counts = take(NB * l->E * 4);
-    w.block_base = take(NB * l->E * 4);
-    w.counts = take(l->E * 4);
-    w.offsets = take((l->E + 1) * 4);
-    w.tile_cum1 = take((l->E + 1) * 4);
-    w.tile_cum2 = take((l->E + 1) * 4);
-    w.full_cum1 = take((l->E + 1) * 4);
-    w.full_cum2 = take((l->E + 1) * 4);
-    w.row_token = take(TK * 4);
-    w.slot_row = take(TK * 4);
-    w.row_weight = take(TK * 4);          // weigh-inputs: routing weight per row
-    w.logits = take(T * l->E * 4);        // router logits when the layer's router runs
-    w.router_grp = take(8 * 4);   // router GEMM: counts, offsets, tile_cum, full_cum
-    // one h-format byte per (GEMM-1 M-tile, GEMM-1 feature tile), worst case
-    // over the two 16-bit kernel variants
-    size_t nfmt = 0;
-    for (GemmKind k : {GemmKind::kPrefill, GemmKind::kDecode, GemmKind::kMid}) {
-        const int64_t ntile = (l->I + gemm_bn(k, true) - 1) / gemm_bn(k, true);
-        const size_t n = (size_t)(max_m_tiles_of(l, T, gemm_bm(k)) * ntile);
-        if (n > nfmt) nfmt = n;
-    }
-    w.hfmt = take(nfmt);
-    w.h = take(TK * l->I * hbytes);
-    w.y = take(TK * l->H * 4);
-    w.total = o;
-    return w;
-}
 
 // Kernel variant: f32 layers use the f32 kernels; otherwise by the average
 // rows per expert: small-M (decode, 32-row) tiles below 96, mid (128-row)
@@ -235,6 +194,80 @@ int path_bn(Path p, bool gated)
 {
     if (p == Path::kF32) return gemm_f32_bn(gated);
     return gemm_bn(kind_of(p), gated);
+}
+
+// Reduction splits of the down GEMM: its tile count (token tiles x feature
+// tiles) can be a few rounds of the device's CUs, leaving the last round
+// mostly idle; splitting its long reduction (I) multiplies the tiles.  The
+// partial sums go to separate f32 buffers that the combine adds in order,
+// so the result stays deterministic.  Worst-case tile count, so the choice
+// depends on (T, geometry) only and the workspace can be sized from it.
+int down_splits(const moe_layer *l, int64_t T, Path path)
+{
+    if (path == Path::kF32) return 1;
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            n > 0)
+            cus = n;
+        else {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+    }
+    const int bm = path_bm(path), bn = path_bn(path, false);
+    const int64_t tiles = max_m_tiles_of(l, T, bm) * ((l->H + bn - 1) / bn);
+    if (tiles == 0 || tiles >= 3 * (int64_t)cus) return 1;
+    const int64_t ksteps = (l->I + 63) / 64;
+    int s = (int)((4 * (int64_t)cus + tiles - 1) / tiles);
+    if (s > 4) s = 4;
+    while (s > 1 && ksteps / s < 16) --s;      // at least 16 k-steps per split
+    return s;
+}
+
+Workspace layout(const moe_layer *l, int64_t T)
+{
+    Workspace w{};
+    const int64_t TK = T * l->K;
+    const int64_t NB = (T + kPermTokens - 1) / kPermTokens;
+    const size_t hbytes = l->wdtype == MOE_DTYPE_F32 ? 4 : 2;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    w.ids = take(TK * 4);
+    w.weights = take(TK * 4);
+    w.block_counts = take(NB * l->E * 4);
+    w.block_base = take(NB * l->E * 4);
+    w.counts = take(l->E * 4);
+    w.offsets = take((l->E + 1) * 4);
+    w.tile_cum1 = take((l->E + 1) * 4);
+    w.tile_cum2 = take((l->E + 1) * 4);
+    w.full_cum1 = take((l->E + 1) * 4);
+    w.full_cum2 = take((l->E + 1) * 4);
+    w.row_token = take(TK * 4);
+    w.slot_row = take(TK * 4);
+    w.row_weight = take(TK * 4);          // weigh-inputs: routing weight per row
+    w.logits = take(T * l->E * 4);        // router logits when the layer's router runs
+    w.router_grp = take(8 * 4);   // router GEMM: counts, offsets, tile_cum, full_cum
+    // one h-format byte per (GEMM-1 M-tile, GEMM-1 feature tile), worst case
+    // over the two 16-bit kernel variants
+    size_t nfmt = 0;
+    for (GemmKind k : {GemmKind::kPrefill, GemmKind::kDecode, GemmKind::kMid}) {
+        const int64_t ntile = (l->I + gemm_bn(k, true) - 1) / gemm_bn(k, true);
+        const size_t n = (size_t)(max_m_tiles_of(l, T, gemm_bm(k)) * ntile);
+        if (n > nfmt) nfmt = n;
+    }
+    w.hfmt = take(nfmt);
+    w.h = take(TK * l->I * hbytes);
+    // y: one [T*K, H] f32 buffer per split of the down GEMM
+    w.y = take(TK * l->H * 4 * down_splits(l, T, choose_path(l, T)));
+    w.total = o;
+    return w;
 }
 
 moe_status hip_check(hipError_t e, const char *what)
@@ -329,6 +362,7 @@ moe_status run_router(const moe_layer *l, const void *x, int64_t T, float *logit
     const Path rp = path == Path::kF32 ? Path::kF32 : Path::kDecode;
     const int bm = path_bm(rp), bn = path_bn(rp, false);
     g.nN = (int)((l->E + bn - 1) / bn);
+    g.ksplit = 1;
     g.out = logits;
     g.w.w_gate = g.w.w_up = l->wr_t;
     g.w.e_rows = l->E;
@@ -778,6 +812,7 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     const int epi1 = gt ? kEpiGated : kEpiAct;
     const int bn1 = path_bn(path, gt);
     g1.nN = (int)((l->I + bn1 - 1) / bn1);
+    g1.ksplit = 1;
     g1.out = wsb + W.h;
     g1.act = l->opts.activation;
     g1.gelu_mode = l->opts.gelu_mode;
@@ -838,6 +873,9 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     const int bn2 = path_bn(path, false);
     g2.nN = (int)((l->H + bn2 - 1) / bn2);
     g2.out = wsb + W.y;
+    const int splits = down_splits(l, T, path);
+    g2.ksplit = splits;
+    g2.split_stride = T * l->K * l->H;
     g2.w.w_gate = l->w.down_experts.data;
     g2.w.s_gate = l->w.down_experts.scales;
     g2.w.e_rows = l->H;
@@ -858,7 +896,7 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
         g2.nrb_half = (int)(l->H / 32);
     }
 
-    if (max_m_tiles * (g1.nN > g2.nN ? g1.nN : g2.nN) + 8 > 0x7fffffffLL)
+    if (max_m_tiles * (g1.nN > g2.nN * splits ? g1.nN : g2.nN * splits) + 8 > 0x7fffffffLL)
         return fail(MOE_ERR_UNSUPPORTED, "problem too large for one launch");
 
     if (path == Path::kF32) {
@@ -888,6 +926,8 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     ca.K = (int)l->K;
     ca.out_bf16 = x->dtype == MOE_DTYPE_BF16;
     ca.unit_weights = l->opts.weigh_inputs;
+    ca.splits = splits;
+    ca.split_stride = g2.split_stride;
     if ((st = hip_check(launch_combine(ca, s), "combine launch"))) return st;
     if ((st = mark(5))) return st;
     return copy_routing(l, T, wsb, W, routing, s);

@@ -26,7 +26,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     for (int j = 0; j < a.K; ++j) {
         const float w = a.unit_weights ? 1.0f : a.weights[(int64_t)t * a.K + j];
         const int row = a.slot_row[(int64_t)t * a.K + j];
-        const f32x4 v = *(const f32x4 *)(a.y + (int64_t)row * a.H + c);
+        // the partial sums of a split down GEMM, added in split order
+        f32x4 v = *(const f32x4 *)(a.y + (int64_t)row * a.H + c);
+        for (int s = 1; s < a.splits; ++s)
+            v += *(const f32x4 *)(a.y + s * a.split_stride + (int64_t)row * a.H + c);
         acc += w * v;
     }
     const int64_t o = (int64_t)t * a.H + c;

@@ -118,7 +118,8 @@ __device__ inline f32x16 mfma(const u32x4 &a, const u32x4 &b, const f32x16 &c)
 //  down / plain: + bias, f32 store.
 template <class TL, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
-                                         f32x16 (&acc)[TL::FN][TL::FM], float *s_red)
+                                         f32x16 (&acc)[TL::FN][TL::FM], float *s_red,
+                                         uint8_t *lds)
 {
     constexpr int NWAVES = TL::NT / 64;
     constexpr bool GATED = EPI == kEpiGated;
@@ -175,34 +176,81 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
         for (int w = 1; w < NWAVES; ++w) bmax = fmaxf(bmax, s_red[w]);
         const bool f16 = g.f16_ok && bmax <= 65504.0f;
         if (tid == 0) g.hfmt[(int64_t)tw.mg * g.h_tiles + tw.nt] = f16 ? kHF16 : kHBF16;
-        // pass 2: store h
+        // pass 2: store h.  When the whole h tile fits in LDS (beside the
+        // reduction scratch), each lane parks its 4 features of a token there
+        // (row pitch padded by 16 bytes: the 32 tokens of a 64-lane write
+        // fall on every bank at most twice), then the workgroup writes whole
+        // 16-byte chunks, a wave covering full row segments -- instead of
+        // 8-byte pieces scattered over 32 rows per store instruction.
+        constexpr int HW = GATED ? TL::BN / 2 : TL::BN;     // h features per tile
+        constexpr int PITCH = HW * 2 + 16;
+        constexpr bool STAGED = 256 + TL::BM * PITCH <= TL::LDS_BYTES;
         uint16_t *h = (uint16_t *)g.out;
+        if constexpr (STAGED) {
+            uint8_t *hs = lds + 256;
+            __syncthreads();                 // every wave has read s_red
 #pragma unroll
-        for (int fp = 0; fp < FH; ++fp)
+            for (int fp = 0; fp < FH; ++fp)
 #pragma unroll
-            for (int m = 0; m < TL::FM; ++m) {
-                const int tl = wm * TL::TM + m * 32 + lrow;
-                if (tl >= tw.nrows) continue;
-                uint16_t *hrow = h + (int64_t)(tw.row0 + tl) * g.Nout;
+                for (int m = 0; m < TL::FM; ++m) {
+                    const int tl = wm * TL::TM + m * 32 + lrow;
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const int c = tw.n0 + wn * WH + fp * 32 + i4 * 8 + fq;
-                    if (c >= g.Nout) continue;
-                    const f32x16 &a = acc[fp][m];
-                    const int r0 = i4 * 4;
-                    if (f16) {
-                        f16x4 o = {(_Float16)a[r0], (_Float16)a[r0 + 1], (_Float16)a[r0 + 2],
-                                   (_Float16)a[r0 + 3]};
-                        *(f16x4 *)(hrow + c) = o;
-                    } else {
-                        bf16x4 o = {(__bf16)a[r0], (__bf16)a[r0 + 1], (__bf16)a[r0 + 2],
-                                    (__bf16)a[r0 + 3]};
-                        *(bf16x4 *)(hrow + c) = o;
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        const int cl = wn * WH + fp * 32 + i4 * 8 + fq;   // feature in tile
+                        const f32x16 &a = acc[fp][m];
+                        const int r0 = i4 * 4;
+                        uint8_t *dst = hs + tl * PITCH + cl * 2;
+                        if (f16) {
+                            f16x4 o = {(_Float16)a[r0], (_Float16)a[r0 + 1], (_Float16)a[r0 + 2],
+                                       (_Float16)a[r0 + 3]};
+                            *(f16x4 *)dst = o;
+                        } else {
+                            bf16x4 o = {(__bf16)a[r0], (__bf16)a[r0 + 1], (__bf16)a[r0 + 2],
+                                        (__bf16)a[r0 + 3]};
+                            *(bf16x4 *)dst = o;
+                        }
                     }
                 }
+            __syncthreads();
+            constexpr int CPRH = HW / 8;                     // 16-byte chunks per h row
+            for (int q = tid; q < TL::BM * CPRH; q += TL::NT) {
+                const int r = q / CPRH, ch = q % CPRH;
+                const int c = tw.n0 + ch * 8;
+                if (r < tw.nrows && c < g.Nout)
+                    *(u32x4 *)(h + (int64_t)(tw.row0 + r) * g.Nout + c) =
+                        *(const u32x4 *)(hs + r * PITCH + ch * 16);
             }
+        } else {
+#pragma unroll
+            for (int fp = 0; fp < FH; ++fp)
+#pragma unroll
+                for (int m = 0; m < TL::FM; ++m) {
+                    const int tl = wm * TL::TM + m * 32 + lrow;
+                    if (tl >= tw.nrows) continue;
+                    uint16_t *hrow = h + (int64_t)(tw.row0 + tl) * g.Nout;
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        const int c = tw.n0 + wn * WH + fp * 32 + i4 * 8 + fq;
+                        if (c >= g.Nout) continue;
+                        const f32x16 &a = acc[fp][m];
+                        const int r0 = i4 * 4;
+                        if (f16) {
+                            f16x4 o = {(_Float16)a[r0], (_Float16)a[r0 + 1], (_Float16)a[r0 + 2],
+                                       (_Float16)a[r0 + 3]};
+                            *(f16x4 *)(hrow + c) = o;
+                        } else {
+                            bf16x4 o = {(__bf16)a[r0], (__bf16)a[r0 + 1], (__bf16)a[r0 + 2],
+                                        (__bf16)a[r0 + 3]};
+                            *(bf16x4 *)(hrow + c) = o;
+                        }
+                    }
+                }
+        }
     } else {
-        float *y = (float *)g.out;
+        // split s of a split reduction writes its partial sums to its own
+        // buffer; the bias goes in once, with split 0
+        float *y = (float *)g.out + (int64_t)tw.ks * g.split_stride;
+        const void *bias = tw.ks == 0 ? g.w.b_gate : nullptr;
         const int64_t eb = (int64_t)tw.e * g.w.e_rows;
 #pragma unroll
         for (int f = 0; f < TL::FN; ++f)
@@ -219,7 +267,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         float v = acc[f][m][i4 * 4 + j];
-                        if (g.w.b_gate) v += bias_at(g.w.b_gate, eb + c + j);
+                        if (bias) v += bias_at(bias, eb + c + j);
                         o[j] = v;
                     }
                     *(f32x4 *)(yrow + c) = o;
@@ -410,12 +458,17 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds_offset(lds) + wave * 1024);
     const uint32_t wave_sc = __builtin_amdgcn_readfirstlane(
         lds_offset(lds) + TL::B_BASE + TL::CODE_BYTES + wave * TL::RBW * 64);
-    const int nk = (Kd + TL::BK - 1) / TL::BK;
-    const int nfull = RAGGED ? Kd / TL::BK : nk;    // k-steps with no chunk past Kd
+    // k-steps [kbeg, kend) of the reduction: all of them, or this tile's
+    // split; kt below counts from kbeg (LDS stages by kt, addresses by kx(kt))
+    const int nk_all = (Kd + TL::BK - 1) / TL::BK;
+    const int kbeg = tw.ks * nk_all / g.ksplit;
+    const int nk = (tw.ks + 1) * nk_all / g.ksplit - kbeg;
+    const int nfull = RAGGED ? Kd / TL::BK : nk_all;   // k-steps with no chunk past Kd
+    auto kx = [&](int kt) { return kt + kbeg; };
     auto issue_a_one = [&](int kt, int i) {
         const uint32_t st = wave_lds + (kt % TL::SA) * TL::A_BYTES;
-        const int k0 = kt * TL::BK;
-        const bool full = kt < nfull;
+        const int k0 = kx(kt) * TL::BK;
+        const bool full = kx(kt) < nfull;
         dma16((!RAGGED || full || k0 + a_k[i] < Kd) ? a_src[i] + 2 * k0 : zero,
               st + i * TL::NWAVES * 1024);
     };
@@ -423,15 +476,15 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     auto issue_b_one = [&](int kt, int i) {
         if constexpr (TL::MX) {
             if (i < TL::NBC) {
-                dma16(b_src[i] + (int64_t)kt * 1024,
+                dma16(b_src[i] + (int64_t)kx(kt) * 1024,
                       wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES + i * TL::NWAVES * 1024);
             } else if (lane < 4 * TL::RBW) {
-                dma16(s_src + (int64_t)kt * 64, wave_sc + (kt % TL::SB) * TL::B_BYTES);
+                dma16(s_src + (int64_t)kx(kt) * 64, wave_sc + (kt % TL::SB) * TL::B_BYTES);
             }
         } else {
             const uint32_t st = wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
-            const int k0 = kt * TL::BK;
-            const bool full = kt < nfull;
+            const int k0 = kx(kt) * TL::BK;
+            const bool full = kx(kt) < nfull;
             dma16((!RAGGED || full || k0 + b_k[i] < Kd) ? b_src[i] + 2 * k0 : zero,
                   st + i * TL::NWAVES * 1024);
         }
@@ -510,7 +563,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
             // token chunk of this sub-step (MXFP4: the permuted k order)
             const int acoff = ((TL::MX ? 4 * lhalf + ks : ks * 2 + lhalf) ^ lsw) * 16;
             // bf16 down GEMM: an fp16-stored h step is rounded to bf16
-            const bool a_f16 = HIN && !F16 && hf[(kt * TL::BK) / g.h_width] == kHF16;
+            const bool a_f16 = HIN && !F16 && hf[(kx(kt) * TL::BK) / g.h_width] == kHF16;
 #pragma unroll
             for (int m = 0; m < MV; ++m) {
                 af[b][m] = *(const u32x4 *)(sa + (wm * TL::TM + m * 32 + lrow) * TL::ROWB + acoff);
@@ -598,7 +651,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     else kloop(std::integral_constant<int, 0>{});
     // all waves are done reading LDS before the epilogue reuses it as scratch
     __syncthreads();
-    epilogue<TL, EPI>(g, tw, acc, s_red);
+    epilogue<TL, EPI>(g, tw, acc, s_red, lds);
 }
 
 // At least two waves per SIMD (256 VGPRs each): the 4-wave MXFP4 mid tile
@@ -648,7 +701,7 @@ __global__ __launch_bounds__(TL::NT, 2) void gemm_dma_kernel(GemmArgs g)
 template <class TL, int EPI>
 hipError_t launch_dma(const GemmArgs &a, int64_t max_m_tiles, hipStream_t s)
 {
-    const int64_t grid = max_m_tiles * a.nN + 8;
+    const int64_t grid = max_m_tiles * a.nN * a.ksplit + 8;
     gemm_dma_kernel<TL, EPI><<<dim3((unsigned)grid), dim3(TL::NT), 0, s>>>(a);
     return hipGetLastError();
 }

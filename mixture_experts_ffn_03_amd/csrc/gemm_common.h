@@ -12,6 +12,7 @@ struct TileWork {
     int e, row0, nrows, n0;
     int mg;      // global M-tile index (tile_cum[e] + token tile)
     int nt;      // feature tile index
+    int ks;      // reduction split (0 .. ksplit-1)
 };
 
 // Map this workgroup to a tile, or return false when it has none.
@@ -40,7 +41,9 @@ __device__ inline bool find_tile(const GemmArgs &g, int *s_cum, int bm, int n_wi
         s_full[i] = g.full_cum[i];
     }
     __syncthreads();
-    const int nN = g.nN;
+    // a split reduction multiplies the feature tiles: tile column
+    // s * nN + nt is split s of feature tile nt
+    const int nN = g.nN * g.ksplit;
     const int F = s_full[g.E] * nN;               // full tiles
     const int P = s_cum[g.E] * nN - F;            // partial tiles (one per expert and N tile)
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -80,8 +83,10 @@ __device__ inline bool find_tile(const GemmArgs &g, int *s_cum, int bm, int n_wi
     w->e = e;
     w->row0 = g.offsets[e] + mtile * bm;
     w->nrows = min(bm, g.counts[e] - mtile * bm);
-    w->n0 = nt * n_width;
     w->mg = s_cum[e] + mtile;
+    w->ks = nt / g.nN;
+    nt -= w->ks * g.nN;
+    w->n0 = nt * n_width;
     w->nt = nt;
     return true;
 }

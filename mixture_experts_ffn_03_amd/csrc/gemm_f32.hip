@@ -90,7 +90,7 @@ int gemm_f32_bn(bool) { return BNF; }
 
 hipError_t launch_gemm_f32(int epi, const GemmArgs &a, int64_t max_m_tiles, hipStream_t s)
 {
-    const int64_t grid = max_m_tiles * a.nN + 8;
+    const int64_t grid = max_m_tiles * a.nN * a.ksplit + 8;
     const dim3 gd((unsigned)grid), bd(NT);
     switch (epi) {
     case kEpiGated: gemm_f32_kernel<kEpiGated><<<gd, bd, 0, s>>>(a); break;

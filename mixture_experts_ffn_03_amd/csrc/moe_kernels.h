@@ -81,6 +81,9 @@ struct GemmArgs {
     int Kd;                      // reduction length
     int Nout;                    // output features: I (gated) or H (down)
     int nN;                      // feature tiles
+    int ksplit;                  // reduction splits (>= 1): split s reduces k-steps
+                                 // [s*nk/ksplit, (s+1)*nk/ksplit) into out + s*split_stride
+    int64_t split_stride;        // elements between the splits' outputs (f32 y only)
     void *out;                   // h bf16 [T*K, I] or y f32 [T*K, H]
     int act;                     // moe_activation code (0..5)
     int gelu_mode;               // 0 erf, 1 tanh
@@ -150,6 +153,8 @@ struct CombineArgs {
     int T, H, K;
     int out_bf16;                // 1: bf16 x/out, 0: f32
     int unit_weights;            // weigh-inputs: every kept output weighs 1
+    int splits;                  // y holds this many partial sums (split reduction),
+    int64_t split_stride;        // split_stride elements apart, summed in order
 };
 
 // Dense f32 grouped GEMM (the fp32 layer): same contract as GemmArgs with

@@ -188,6 +188,8 @@ def test_forward_argument_errors_before_launch(L):
 
 def test_workspace_grows_with_tokens(L):
     st, h = create(L)
+    z = C.c_size_t()
+    assert L.lib().moe_workspace_size(h, 0, C.byref(z)) == 0     # T = 0 is a valid size query
     a, b = C.c_size_t(), C.c_size_t()
     L.lib().moe_workspace_size(h, 10, C.byref(a))
     L.lib().moe_workspace_size(h, 1000, C.byref(b))

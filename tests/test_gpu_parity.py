@@ -243,3 +243,19 @@ def test_full_size_sampled(name, n):
     assert (ref["ids"] == ro["ids"][toks]).all()
     compare_out(out[torch.as_tensor(toks, device=out.device)], ref["out"], cfg.x_dtype,
                 f"{name} full size, {len(toks)} tokens")
+
+
+@pytest.mark.parametrize("I", [2304, 4096])
+@pytest.mark.parametrize("w_dtype,variant", [("bf16", 1), ("bf16", 3), ("mxfp4", 0),
+                                             ("bf16", 2)])
+def test_split_down_gemm(I, w_dtype, variant):
+    """Few down-GEMM tiles and a long reduction: the down GEMM splits I into
+    2 (I=2304) or 4 (I=4096) parts whose partial sums the combine adds in
+    order; with biases, which only the first split may add."""
+    cfg = synth.MoeConfig(name="split", cid=205, T=300, H=512, I=I, E=4, K=2,
+                          w_dtype=w_dtype, layout="interleaved", expert_biases=True,
+                          bias_std=0.5)
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, _ = run_gpu(cfg, inp, gemm_variant=variant)
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"split down I={I} {w_dtype} v{variant}")
