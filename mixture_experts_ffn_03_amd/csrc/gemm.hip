@@ -404,6 +404,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     // ---- per-load global sources of the token rows: row base + swizzled chunk
     const uint8_t *a_src[TL::NA];
     int a_k[TL::NA];                   // first k of the chunk this load fetches
+    bool a_ok[TL::NA];                 // the chunk's row holds a token
 #pragma unroll
     for (int i = 0; i < TL::NA; ++i) {
         const int q = (i * TL::NWAVES + wave) * 64 + lane;   // LDS chunk index
@@ -412,6 +413,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
         const int r = tw.row0 + min(row, tw.nrows - 1);
         const int src = g.row_token ? g.row_token[r] : r;
         a_k[i] = c * 8;
+        a_ok[i] = row < tw.nrows;
         a_src[i] = (const uint8_t *)g.a + ((int64_t)src * Kd + c * 8) * 2;
     }
     // ---- weight sources.  16-bit: row base + swizzled chunk.  MXFP4: this
@@ -469,8 +471,13 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
         const uint32_t st = wave_lds + (kt % TL::SA) * TL::A_BYTES;
         const int k0 = kx(kt) * TL::BK;
         const bool full = kx(kt) < nfull;
-        dma16((!RAGGED || full || k0 + a_k[i] < Kd) ? a_src[i] + 2 * k0 : zero,
-              st + i * TL::NWAVES * 1024);
+        // rows past the tile's tokens are not fetched (their LDS rows only
+        // feed output columns the epilogue drops).  Only token loads are
+        // ever skipped, so every wait below, which counts the weight loads
+        // issued after a step's token loads, still covers what it must.
+        if (a_ok[i])
+            dma16((!RAGGED || full || k0 + a_k[i] < Kd) ? a_src[i] + 2 * k0 : zero,
+                  st + i * TL::NWAVES * 1024);
     };
     // weight load i of step kt (MXFP4: i == NBC is the scale load)
     auto issue_b_one = [&](int kt, int i) {
