@@ -91,18 +91,26 @@ __device__ inline bool find_tile(const GemmArgs &g, int *s_cum, int bm, int n_wi
     return true;
 }
 
+// sigmoid(v) = 1 / (1 + e^-v) with the hardware exponential and reciprocal
+// (each within ~1 ulp of f32; h is stored in 16 bits, 2^-11 at best), instead
+// of an IEEE division sequence per value.  v -> -inf gives rcp(inf) = 0.
+__device__ inline float sigmoid_fast(float v)
+{
+    return __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+}
+
 // Gated activation in fp32.  act 0: SiLU-gated, h = g*sigmoid(g)*u.
 // act 1: clamped SwiGLU, g' = min(g, L), u' = clamp(u, -L, L) when L > 0,
 // h = g'*sigmoid(alpha*g')*(u' + beta).
 __device__ inline float gated_act(int act, float g, float u, float alpha,
                                   float beta, float limit)
 {
-    if (act == 0) return g * (1.0f / (1.0f + __expf(-g))) * u;
+    if (act == 0) return g * sigmoid_fast(g) * u;
     if (limit > 0.0f) {
         g = fminf(g, limit);
         u = fminf(fmaxf(u, -limit), limit);
     }
-    return g * (1.0f / (1.0f + __expf(-alpha * g))) * (u + beta);
+    return g * sigmoid_fast(alpha * g) * (u + beta);
 }
 
 // Activation of a non-gated expert's fc1 output (act 2 relu, 3 gelu in the
@@ -115,7 +123,7 @@ __device__ inline float single_act(int act, int gelu_mode, float v)
         if (gelu_mode == 1)
             return 0.5f * v * (1.0f + tanhf(0.7978845608f * (v + 0.044715f * v * v * v)));
         return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
-    case 4: return v * (1.0f / (1.0f + __expf(-v)));
+    case 4: return v * sigmoid_fast(v);
     default: return v;
     }
 }
