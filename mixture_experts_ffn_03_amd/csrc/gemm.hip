@@ -308,9 +308,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
 // fragments to bf16.  Token chunks past the reduction length are read from a
 // zero buffer; packed MXFP4 weights are zero past it already.
 
-template <int BN_, int BM_, int BK_, int WN_, int WM_, int SA_, int SB_, bool MX_>
+template <int BN_, int BM_, int BK_, int WN_, int WM_, int SA_, int SB_, bool MX_, int WPE_ = 2>
 struct DTile {
     static constexpr int BN = BN_, BM = BM_, BK = BK_, WN = WN_, WM = WM_;
+    // waves per SIMD the registers are budgeted for: 2 (256 each), or 1 (512:
+    // the 128 x 128 accumulators of a 4-wave 256 x 256 tile)
+    static constexpr int WPE = WPE_;
     static constexpr int SA = SA_, SB = SB_;            // LDS stages of A and of B
     static constexpr bool MX = MX_;                     // MXFP4 weights (packed)
     static constexpr int NT = 64 * WN * WM;
@@ -351,6 +354,11 @@ struct DTile {
 // piece halves the L2->LDS rate); A (token rows, L2/MALL resident) two
 // stages, B (weights, first touch from HBM) three: 2 x 32 + 3 x 32 KiB.
 using PrefillDTile = DTile<256, 256, 64, 4, 2, 2, 3, false>;
+// The same tile and stages for the gate||up (and fc1) GEMM on 256 threads:
+// one wave per SIMD with a 128 x 128 wave tile (a third less LDS read per
+// MFMA than 64 x 128), its MFMAs interleaved by hand with the reads and
+// loads (kloop_il below).
+using PrefillFcTile = DTile<256, 256, 64, 2, 2, 2, 3, false, 1>;
 // 256 threads, wave 64x32; weights stream from HBM: four B stages.
 using DecodeDTile = DTile<256, 32, 64, 4, 1, 2, 4, false>;
 // MXFP4 weights: a weight stage is 8.5 KiB, so four of them fit beside the
@@ -495,6 +503,32 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
             dma16((!RAGGED || full || k0 + b_k[i] < Kd) ? b_src[i] + 2 * k0 : zero,
                   st + i * TL::NWAVES * 1024);
         }
+    };
+    // Branch-free forms for the interleaved loop.  A token row past the
+    // tile fetches the 16 zero bytes at every step (its step is 0 bytes); a
+    // step past the last one fetches the last step again (L2 hits) into its
+    // free stage; so every k-step issues the same loads, the address is one
+    // multiply-add, and the waits need no cases.
+    const uint8_t *a_base[TL::NA];
+    uint32_t a_step[TL::NA];
+#pragma unroll
+    for (int i = 0; i < TL::NA; ++i) {
+        a_base[i] = a_ok[i] ? a_src[i] : zero;
+        a_step[i] = a_ok[i] ? 2 * TL::BK : 0;
+    }
+    auto issue_a_nb = [&](int kt, int i) {
+        const uint32_t st = wave_lds + (kt % TL::SA) * TL::A_BYTES;
+        const uint32_t kc = (uint32_t)(kbeg + min(kt, nk - 1));
+        const uint8_t *p = a_base[i] + (uint64_t)kc * a_step[i];
+        if (RAGGED) p = ((int)kc * TL::BK + a_k[i] < Kd) ? p : zero;
+        dma16(p, st + i * TL::NWAVES * 1024);
+    };
+    auto issue_b_nb = [&](int kt, int i) {
+        const uint32_t st = wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
+        const uint32_t kc = (uint32_t)(kbeg + min(kt, nk - 1));
+        const uint8_t *p = b_src[i] + (uint64_t)kc * (2 * TL::BK);
+        if (RAGGED) p = ((int)kc * TL::BK + b_k[i] < Kd) ? p : zero;
+        dma16(p, st + i * TL::NWAVES * 1024);
     };
     auto issue_a = [&](int kt) {
 #pragma unroll
@@ -649,8 +683,112 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
             }
         }
     };
+    // One wave per SIMD: the wave itself keeps the matrix pipe fed, so its
+    // instruction stream is laid out by hand (each sched_barrier fences the
+    // compiler's scheduler).  In sub-steps 0 .. NKS-2 every MFMA is followed
+    // by one item: a fragment read of the next sub-step, then a DMA load of
+    // the step's group (A(kt+1), then B(kt+SB-1)), so the whole group goes
+    // out before the last sub-step.  The last sub-step issues one MFMA, then
+    // the step barrier (its own fragments were read in the sub-step before),
+    // then the next step's reads between its remaining MFMAs.
+    auto kloop_il = [&](auto mv_tag) {
+        constexpr int MV = decltype(mv_tag)::value;
+        u32x4 bf[2][TL::FN], af[2][TL::FM > 0 ? TL::FM : 1];
+        auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+        // fragment r of sub-step (kt, ks) into buffer b: weights r < FN,
+        // then tokens FN + m
+        auto read_one = [&](int kt, int ks, int b, int r) {
+            const uint8_t *sa = lds + (kt % TL::SA) * TL::A_BYTES;
+            const uint8_t *sb = lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
+            const int coff = ((ks * 2 + lhalf) ^ lsw) * 16;
+            if (r < TL::FN) {
+                bf[b][r] = *(const u32x4 *)(sb + (brow(r) + lrow) * TL::ROWB + coff);
+                if (F16) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) bf[b][r][w] = bf16x2_to_f16x2(bf[b][r][w]);
+                }
+            } else {
+                const int m = r - TL::FN;
+                af[b][m] = *(const u32x4 *)(sa + (wm * TL::TM + m * 32 + lrow) * TL::ROWB + coff);
+                if (HIN && !F16 && hf[(kx(kt) * TL::BK) / g.h_width] == kHF16) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) af[b][m][w] = f16x2_to_bf16x2(af[b][m][w]);
+                }
+            }
+        };
+        constexpr int NR = TL::FN + MV;                // reads per sub-step
+        constexpr int L = TL::NA + TL::NB;             // loads per k-step
+        constexpr int Q = TL::FN * MV;                 // MFMAs per sub-step
+        // load q of step j's group
+        auto load_one = [&](int j, int q) {
+            if (q < TL::NA) issue_a_nb(j + 1, q);
+            else issue_b_nb(j + TL::SB - 1, q - TL::NA);
+        };
+        auto mfma_q = [&](int cur, int q) {
+            const int f = q / (MV > 0 ? MV : 1), m = q % (MV > 0 ? MV : 1);
+            acc[f][m] = mfma<F16>(bf[cur][f], af[cur][m], acc[f][m]);
+        };
+        // prologue: B(0), A(0), B(1 .. SB-2); A(0) and B(0) landed
+#pragma unroll
+        for (int i = 0; i < TL::NB; ++i) issue_b_nb(0, i);
+#pragma unroll
+        for (int i = 0; i < TL::NA; ++i) issue_a_nb(0, i);
+#pragma unroll
+        for (int s = 1; s < TL::SB - 1; ++s)
+#pragma unroll
+            for (int i = 0; i < TL::NB; ++i) issue_b_nb(s, i);
+        wait_loads_barrier<(TL::SB - 2) * TL::NB>();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
+        fence();
+        for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int cur = ks & 1;
+                const int l0 = ks * L / (NKS - 1), l1 = (ks + 1) * L / (NKS - 1);
+                if (ks + 1 < NKS) {
+                    constexpr int NI = NR + (L + NKS - 2) / (NKS - 1);
+#pragma unroll
+                    for (int i = 0; i < (Q > NI ? Q : NI); ++i) {
+                        if (i < Q) mfma_q(cur, i);
+                        if (i < NR) read_one(kt, ks + 1, cur ^ 1, i);
+                        else if (i - NR < l1 - l0) load_one(kt, l0 + i - NR);
+                        fence();
+                    }
+                } else {
+                    constexpr int PRE = Q > 0 ? 1 : 0;
+                    if (PRE) mfma_q(cur, 0);
+                    fence();
+                    // A(kt+1) and B(kt+1) landed: only B(kt+SB-1) may be pending
+                    if (kt + 1 < nk) wait_loads_barrier<TL::SB >= 3 ? TL::NB : 0>();
+                    fence();
+                    // (past the last step these read a stale stage into the
+                    // idle buffer: in bounds and never used)
+#pragma unroll
+                    for (int i = 0; i < (Q - PRE > NR ? Q - PRE : NR); ++i) {
+                        if (i < Q - PRE) mfma_q(cur, PRE + i);
+                        if (i < NR) read_one(kt + 1, 0, cur ^ 1, i);
+                        fence();
+                    }
+                }
+            }
+        }
+    };
     // every wave runs the same loads and barriers; only its MFMA work differs
     const int mv = min(max((tw.nrows - wm * TL::TM + 31) / 32, 0), TL::FM);
+    if constexpr (TL::WPE == 1) {
+        static_assert(!TL::MX && TL::SB >= 3 && NKS >= 2, "interleaved loop: 16-bit weights");
+        if (mv == TL::FM) kloop_il(std::integral_constant<int, TL::FM>{});
+        else if (TL::FM > 1 && mv == 1) kloop_il(std::integral_constant<int, 1>{});
+        else if (TL::FM > 2 && mv == 2) kloop_il(std::integral_constant<int, (TL::FM > 2 ? 2 : 1)>{});
+        else if (TL::FM > 3 && mv == 3) kloop_il(std::integral_constant<int, (TL::FM > 3 ? 3 : 1)>{});
+        else kloop_il(std::integral_constant<int, 0>{});
+        // the repeated loads past the last step land before LDS is reused
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        epilogue<TL, EPI>(g, tw, acc, s_red, lds);
+        return;
+    }
     if (mv == TL::FM) kloop(std::integral_constant<int, TL::FM>{});
     else if (TL::FM > 1 && mv == 1) kloop(std::integral_constant<int, 1>{});
     else if (TL::FM > 2 && mv == 2) kloop(std::integral_constant<int, (TL::FM > 2 ? 2 : 1)>{});
@@ -661,10 +799,10 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     epilogue<TL, EPI>(g, tw, acc, s_red, lds);
 }
 
-// At least two waves per SIMD (256 VGPRs each): the 4-wave MXFP4 mid tile
-// then runs two workgroups per CU.
+// Registers for TL::WPE waves per SIMD: with 2 (256 VGPRs each) the 4-wave
+// MXFP4 mid tile runs two workgroups per CU; the 4-wave fc tile takes 512.
 template <class TL, int EPI>
-__global__ __launch_bounds__(TL::NT, 2) void gemm_dma_kernel(GemmArgs g)
+__global__ __launch_bounds__(TL::NT, TL::WPE) void gemm_dma_kernel(GemmArgs g)
 {
     constexpr int NW = EPI == kEpiGated ? TL::BN / 2 : TL::BN;
     // one LDS allocation: the scheduling table, then the stages, then the
@@ -674,7 +812,7 @@ __global__ __launch_bounds__(TL::NT, 2) void gemm_dma_kernel(GemmArgs g)
     float *s_red = (float *)lds;
 
     TileWork tw;
-    if (!find_tile(g, s_cum, TL::BM, NW, &tw)) return;
+    if (!find_tile(g, s_cum, NW, &tw)) return;
     const bool ragged = g.Kd % TL::BK != 0;
     if constexpr (EPI == kEpiDown) {
         // down GEMM: fp16 operands iff every h tile of these rows is fp16
@@ -832,8 +970,10 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, bool mxfp4, const GemmArgs &
     if (mxfp4 && epi == kEpiPlain) return hipErrorInvalidValue;   // router weights are 16-bit
     switch (kind) {
     case GemmKind::kPrefill:
-        return mxfp4 ? launch_epi<PrefillMXTile>(epi, a, max_m_tiles, s)
-                     : launch_epi<PrefillDTile>(epi, a, max_m_tiles, s);
+        if (mxfp4) return launch_epi<PrefillMXTile>(epi, a, max_m_tiles, s);
+        if (epi == kEpiGated) return launch_dma<PrefillFcTile, kEpiGated>(a, max_m_tiles, s);
+        if (epi == kEpiAct) return launch_dma<PrefillFcTile, kEpiAct>(a, max_m_tiles, s);
+        return launch_epi<PrefillDTile>(epi, a, max_m_tiles, s);
     case GemmKind::kMid:
         return mxfp4 ? launch_epi<MidMXTile>(epi, a, max_m_tiles, s)
                      : launch_epi<MidDTile>(epi, a, max_m_tiles, s);

@@ -17,13 +17,18 @@ struct TileWork {
 
 // Map this workgroup to a tile, or return false when it has none.
 //
-// Two classes of tiles: full ones (bm rows) and each expert's last, partial
-// one.  Full tiles all take the same time, so the workgroups that share a
-// weight panel or a token block run side by side and the XCD's L2 serves
-// the repeats of each k-slice; a partial tile skips its empty row blocks and
-// finishes early, and interleaved with full tiles it would let its CU run
-// ahead and scatter the sharers apart in time (measured: about twice the
-// memory traffic).  So every full tile comes first, the partial ones last.
+// An expert with n >= bm rows has ceil(n / bm) M-tiles and its rows are
+// spread evenly over them (tile t holds rows [t n / m, (t+1) n / m)): its
+// tiles then take the same time, so those that share a weight panel run
+// side by side and the XCD's L2 serves the repeats of each k-slice, and no
+// short remainder tile streams the whole panel again for a few rows (with
+// bm-row tiles plus a remainder, tiles of 1..32 rows took 0.6 of a full
+// tile's time, and 10% of the GEMM).  These tiles form the full class; an
+// expert with fewer than bm rows has one partial tile, which skips its
+// empty row blocks and finishes early: interleaved with full tiles it would
+// let its CU run ahead and scatter the sharers apart in time (measured:
+// about twice the memory traffic).  So every full tile comes first, the
+// partial ones last.
 // Within each class tiles are numbered expert-major, then feature tile, then
 // token tile, so the token tiles that share one expert's weight panel are
 // consecutive.  Hardware dispatches workgroup b to XCD b % 8; each class is
@@ -32,8 +37,7 @@ struct TileWork {
 // then its partial chunk.  The count of tiles is data dependent: the
 // prefix sums are staged in LDS, and surplus workgroups of the worst-case
 // grid return at once.
-__device__ inline bool find_tile(const GemmArgs &g, int *s_cum, int bm, int n_width,
-                                 TileWork *w)
+__device__ inline bool find_tile(const GemmArgs &g, int *s_cum, int n_width, TileWork *w)
 {
     int *s_full = s_cum + g.E + 1;
     for (int i = threadIdx.x; i <= g.E; i += blockDim.x) {
@@ -76,13 +80,17 @@ __device__ inline bool find_tile(const GemmArgs &g, int *s_cum, int bm, int n_wi
         }
         e = lo;
         nt = v - (s_cum[e] - s_full[e]) * nN;
-        mtile = s_full[e + 1] - s_full[e];        // the last M-tile of expert e
+        mtile = 0;                                // the expert's only tile
     } else {
         return false;
     }
+    // rows of M-tile mtile of the expert's ntl tiles
+    const int ntl = s_cum[e + 1] - s_cum[e], cnt = g.counts[e];
+    const int r0 = (int)((int64_t)mtile * cnt / ntl);
+    const int r1 = (int)((int64_t)(mtile + 1) * cnt / ntl);
     w->e = e;
-    w->row0 = g.offsets[e] + mtile * bm;
-    w->nrows = min(bm, g.counts[e] - mtile * bm);
+    w->row0 = g.offsets[e] + r0;
+    w->nrows = r1 - r0;
     w->mg = s_cum[e] + mtile;
     w->ks = nt / g.nN;
     nt -= w->ks * g.nN;

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmArgs g)
     __shared__ float Bs[NB][BK + 1];
     __shared__ int s_cum[2 * (kMaxExperts + 1)];
     TileWork tw;
-    if (!find_tile(g, s_cum, BM, BNF, &tw)) return;
+    if (!find_tile(g, s_cum, BNF, &tw)) return;
     const int tid = threadIdx.x, Kd = g.Kd;
     const float *A = (const float *)g.a;
     const int64_t eb = (int64_t)tw.e * g.w.e_rows;

@@ -37,7 +37,7 @@ struct PermuteArgs {
     int32_t *slot_row;       // [T*K]
     int32_t *tile_cum1;      // [E + 1] cumulative M-tiles of GEMM 1
     int32_t *tile_cum2;      // [E + 1] cumulative M-tiles of GEMM 2
-    int32_t *full_cum1;      // [E + 1] cumulative full (bm-row) M-tiles of GEMM 1
+    int32_t *full_cum1;      // [E + 1] cumulative M-tiles of experts with >= bm rows, GEMM 1
     int32_t *full_cum2;      // [E + 1] same for GEMM 2
     int bm1, bm2;            // token-tile heights of the two GEMMs
     const float *weights;    // [T, K] routing weights, read when row_weight is set
@@ -76,7 +76,7 @@ struct GemmArgs {
     const int32_t *counts;       // [E]
     const int32_t *offsets;      // [E + 1]
     const int32_t *tile_cum;     // [E + 1] cumulative M-tiles at this BM
-    const int32_t *full_cum;     // [E + 1] cumulative full (BM-row) M-tiles
+    const int32_t *full_cum;     // [E + 1] cumulative M-tiles of experts with >= BM rows
     int E;
     int Kd;                      // reduction length
     int Nout;                    // output features: I (gated) or H (down)
@@ -176,7 +176,7 @@ hipError_t launch_gemm_f32(int epi, const GemmArgs &a, int64_t max_m_tiles,
                            hipStream_t s);
 
 // One group of T rows (the router GEMM): counts = {T}, offsets = {0, T},
-// tile_cum = {0, ceil(T / bm)}, full_cum = {0, T / bm}.
+// tile_cum = {0, ceil(T / bm)}, full_cum = {0, T >= bm ? ceil(T / bm) : 0}.
 hipError_t launch_single_group(int32_t *counts, int32_t *offsets, int32_t *tile_cum,
                                int32_t *full_cum, int T, int bm, hipStream_t s);
 // Wr [H, E] -> its transpose [E, H] (elem_bytes 2 or 4).

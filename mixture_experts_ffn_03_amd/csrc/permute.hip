@@ -83,8 +83,11 @@ __global__ __launch_bounds__(1024) void scan_kernel(PermuteArgs a)
     const int off = block_exclusive_scan(e < a.E ? run : 0, buf, &total);
     const int mt1 = e < a.E ? (run + a.bm1 - 1) / a.bm1 : 0;
     const int mt2 = e < a.E ? (run + a.bm2 - 1) / a.bm2 : 0;
-    const int ft1 = e < a.E ? run / a.bm1 : 0;     // full M-tiles
-    const int ft2 = e < a.E ? run / a.bm2 : 0;
+    // M-tiles of the full class: every tile of an expert with at least bm
+    // rows (the GEMMs spread its rows evenly over them); an expert with
+    // fewer rows has one partial tile
+    const int ft1 = run >= a.bm1 ? mt1 : 0;
+    const int ft2 = run >= a.bm2 ? mt2 : 0;
     int tot1, tot2, ftot1, ftot2;
     const int cum1 = block_exclusive_scan(mt1, buf, &tot1);
     const int cum2 = block_exclusive_scan(mt2, buf, &tot2);

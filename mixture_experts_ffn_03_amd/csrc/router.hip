@@ -37,7 +37,7 @@ __global__ void single_group_kernel(int32_t *counts, int32_t *offsets, int32_t *
         tile_cum[0] = 0;
         tile_cum[1] = (T + bm - 1) / bm;
         full_cum[0] = 0;
-        full_cum[1] = T / bm;
+        full_cum[1] = T >= bm ? (T + bm - 1) / bm : 0;
     }
 }
 
