@@ -55,6 +55,9 @@ __device__ inline float bias_at(const void *b, int64_t i)
     return bf16_bits_to_float(((const uint16_t *)b)[i]);
 }
 
+// stands in for an absent bias (read at index 0)
+__device__ const uint16_t g_zero_bias[1] = {0};
+
 // e8m0 byte -> the fp32 multiplier 2^(X-127) (X = 0 is 2^-127, 255 is NaN).
 __device__ inline float e8m0_scale(uint32_t x)
 {
@@ -131,40 +134,98 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
         // features of the h tile held per wave: gate/up pairs, or every block
         constexpr int FH = GATED ? TL::FN / 2 : TL::FN;
         constexpr int WH = GATED ? TL::TN / 2 : TL::TN;
-        // pass 1: activation into the (gate) accumulators, tile max |h|
+        // pass 1: activation into the (gate) accumulators, tile max |h|.
+        // The activation is uniform, so each one gets its own unrolled loop:
+        // tested per value (with the bias tests) it cost as much as the rest
+        // of the epilogue together.  Biases are read once per feature; an
+        // absent one reads a zero, and a column past Nout reads the last
+        // feature's (its value is never stored or counted in the max).  The
+        // gated loops also come in a no-bias form (the bias reads cost 2% of
+        // a Mixtral-shaped gate||up GEMM).
         const int64_t eb = (int64_t)tw.e * g.w.e_rows;
-        float hmax = 0.0f;
+        float rs[TL::FM];
+        bool tok_ok[TL::FM];
 #pragma unroll
         for (int m = 0; m < TL::FM; ++m) {
             const int tl = wm * TL::TM + m * 32 + lrow;
-            const bool tok_ok = tl < tw.nrows;
-            const float rs = (g.row_w && tok_ok) ? g.row_w[tw.row0 + tl] : 1.0f;
+            tok_ok[m] = tl < tw.nrows;
+            rs[m] = (g.row_w && tok_ok[m]) ? g.row_w[tw.row0 + tl] : 1.0f;
+        }
+        const uint16_t *bgp = g.w.b_gate ? (const uint16_t *)g.w.b_gate : g_zero_bias;
+        const uint16_t *bup = (GATED && g.w.b_up) ? (const uint16_t *)g.w.b_up : g_zero_bias;
+        const int64_t bgs = g.w.b_gate ? 1 : 0, bus = (GATED && g.w.b_up) ? 1 : 0;
+        auto pass1 = [&](auto bias_tag, auto act) {
+            constexpr bool BIAS = decltype(bias_tag)::value;
+            float hm = 0.0f;
 #pragma unroll
             for (int fp = 0; fp < FH; ++fp)
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
                     const int c = tw.n0 + wn * WH + fp * 32 + i4 * 8 + fq;
-                    const bool ok = tok_ok && c < g.Nout;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        float gv = acc[fp][m][i4 * 4 + j] * rs;
-                        if (ok && g.w.b_gate)
-                            gv += bias_at(g.w.b_gate,
-                                          eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_gate);
-                        float h;
-                        if constexpr (GATED) {
-                            float uv = acc[fp + TL::FN / 2][m][i4 * 4 + j] * rs;
-                            if (ok && g.w.b_up)
-                                uv += bias_at(g.w.b_up,
-                                              eb + (int64_t)(c + j) * g.w.row_mul + g.w.off_up);
-                            h = gated_act(g.act, gv, uv, g.alpha, g.beta, g.limit);
-                        } else {
-                            h = single_act(g.act, g.gelu_mode, gv);
+                        const bool c_ok = c + j < g.Nout;
+                        float bg = 0.0f, bu = 0.0f;
+                        if constexpr (BIAS) {
+                            const int64_t f = eb + (int64_t)min(c + j, g.Nout - 1) * g.w.row_mul;
+                            bg = bf16_bits_to_float(bgp[(f + g.w.off_gate) * bgs]);
+                            if constexpr (GATED) bu = bf16_bits_to_float(bup[(f + g.w.off_up) * bus]);
                         }
-                        acc[fp][m][i4 * 4 + j] = h;
-                        if (ok) hmax = fmaxf(hmax, fabsf(h));
+#pragma unroll
+                        for (int m = 0; m < TL::FM; ++m) {
+                            float gv = acc[fp][m][i4 * 4 + j] * rs[m];
+                            if constexpr (BIAS) gv += bg;
+                            float uv = 0.0f;
+                            if constexpr (GATED) {
+                                uv = acc[fp + TL::FN / 2][m][i4 * 4 + j] * rs[m];
+                                if constexpr (BIAS) uv += bu;
+                            }
+                            const float h = act(gv, uv);
+                            acc[fp][m][i4 * 4 + j] = h;
+                            hm = fmaxf(hm, (c_ok && tok_ok[m]) ? fabsf(h) : 0.0f);
+                        }
                     }
                 }
+            return hm;
+        };
+        const bool bias = bgs != 0 || bus != 0;
+        auto run = [&](auto act) {
+            if constexpr (GATED)
+                return bias ? pass1(std::true_type{}, act) : pass1(std::false_type{}, act);
+            else
+                return pass1(std::true_type{}, act);
+        };
+        float hmax;
+        if constexpr (GATED) {
+            if (g.act == 0) {
+                hmax = run([](float x, float u) { return x * sigmoid_fast(x) * u; });
+            } else {
+                const float al = g.alpha, be = g.beta, L = g.limit;
+                if (L > 0.0f)
+                    hmax = run([=](float x, float u) {
+                        x = fminf(x, L);
+                        u = fminf(fmaxf(u, -L), L);
+                        return x * sigmoid_fast(al * x) * (u + be);
+                    });
+                else
+                    hmax = run([=](float x, float u) { return x * sigmoid_fast(al * x) * (u + be); });
+            }
+        } else {
+            switch (g.act) {
+            case 2: hmax = run([](float x, float) { return fmaxf(x, 0.0f); }); break;
+            case 3:
+                if (g.gelu_mode == 1)
+                    hmax = run([](float x, float) {
+                        return 0.5f * x * (1.0f + tanhf(0.7978845608f * (x + 0.044715f * x * x * x)));
+                    });
+                else
+                    hmax = run([](float x, float) {
+                        return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+                    });
+                break;
+            case 4: hmax = run([](float x, float) { return x * sigmoid_fast(x); }); break;
+            default: hmax = run([](float x, float) { return x; });
+            }
         }
         // block max -> storage format of this h tile
 #pragma unroll
