@@ -416,10 +416,13 @@ struct DTile {
 // stages, B (weights, first touch from HBM) three: 2 x 32 + 3 x 32 KiB.
 using PrefillDTile = DTile<256, 256, 64, 4, 2, 2, 3, false>;
 // The same tile and stages for the gate||up (and fc1) GEMM on 256 threads:
-// one wave per SIMD with a 128 x 128 wave tile (a third less LDS read per
-// MFMA than 64 x 128), its MFMAs interleaved by hand with the reads and
-// loads (kloop_il below).
-using PrefillFcTile = DTile<256, 256, 64, 2, 2, 2, 3, false, 1>;
+// one wave per SIMD, each 64 features x all 256 token rows (accumulators in
+// AGPRs), its MFMAs interleaved by hand with the reads and loads (kloop_il
+// below).  Every wave spans the tile's rows, so a tile of n rows keeps all
+// four SIMDs at ceil(n / 32) row blocks (a 2 x 2 layout of 128 x 128 waves
+// reads less LDS per MFMA but leaves the SIMDs of the lower half idle or
+// short on a partial tile).
+using PrefillFcTile = DTile<256, 256, 64, 4, 1, 2, 3, false, 1>;
 // 256 threads, wave 64x32; weights stream from HBM: four B stages.
 using DecodeDTile = DTile<256, 32, 64, 4, 1, 2, 4, false>;
 // MXFP4 weights: a weight stage is 8.5 KiB, so four of them fit beside the
@@ -839,11 +842,19 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     const int mv = min(max((tw.nrows - wm * TL::TM + 31) / 32, 0), TL::FM);
     if constexpr (TL::WPE == 1) {
         static_assert(!TL::MX && TL::SB >= 3 && NKS >= 2, "interleaved loop: 16-bit weights");
-        if (mv == TL::FM) kloop_il(std::integral_constant<int, TL::FM>{});
-        else if (TL::FM > 1 && mv == 1) kloop_il(std::integral_constant<int, 1>{});
-        else if (TL::FM > 2 && mv == 2) kloop_il(std::integral_constant<int, (TL::FM > 2 ? 2 : 1)>{});
-        else if (TL::FM > 3 && mv == 3) kloop_il(std::integral_constant<int, (TL::FM > 3 ? 3 : 1)>{});
-        else kloop_il(std::integral_constant<int, 0>{});
+        // every count of 32-row blocks up to FM has its own loop
+        static_assert(TL::FM <= 8, "block counts");
+        switch (mv) {
+        case 1: kloop_il(std::integral_constant<int, 1>{}); break;
+        case 2: kloop_il(std::integral_constant<int, (TL::FM >= 2 ? 2 : 1)>{}); break;
+        case 3: kloop_il(std::integral_constant<int, (TL::FM >= 3 ? 3 : 1)>{}); break;
+        case 4: kloop_il(std::integral_constant<int, (TL::FM >= 4 ? 4 : 1)>{}); break;
+        case 5: kloop_il(std::integral_constant<int, (TL::FM >= 5 ? 5 : 1)>{}); break;
+        case 6: kloop_il(std::integral_constant<int, (TL::FM >= 6 ? 6 : 1)>{}); break;
+        case 7: kloop_il(std::integral_constant<int, (TL::FM >= 7 ? 7 : 1)>{}); break;
+        case 8: kloop_il(std::integral_constant<int, (TL::FM >= 8 ? 8 : 1)>{}); break;
+        default: kloop_il(std::integral_constant<int, 0>{});
+        }
         // the repeated loads past the last step land before LDS is reused
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
