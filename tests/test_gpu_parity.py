@@ -157,6 +157,25 @@ def test_all_tokens_on_one_expert(variant):
     compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"skew variant {variant}")
 
 
+@pytest.mark.parametrize("H", [256, 200])
+@pytest.mark.parametrize("variant", [0, 1])
+def test_tile_row_splits(H, variant):
+    """Expert row counts on both sides of the 256-row tile: 256 (one full
+    tile), 257 (two tiles of 128 and 129 rows), 513 (three of 171) and 31 (a
+    single partial tile), so the gate||up GEMM runs its loops for 1, 4, 5, 6
+    and 8 row blocks; H = 200 adds a ragged reduction."""
+    counts = [256, 257, 513, 31]
+    cfg = synth.MoeConfig(name="rows", cid=209, T=sum(counts), H=H, I=192, E=4, K=1)
+    inp = synth.make_inputs(cfg, device=DEV)
+    owner = np.repeat(np.arange(4), counts)
+    owner = owner[np.random.default_rng(209).permutation(cfg.T)]
+    inp["logits"][torch.arange(cfg.T, device=DEV), torch.from_numpy(owner).to(DEV)] += 30.0
+    out, r, _ = run_gpu(cfg, inp, gemm_variant=variant)
+    assert list(r["expert_counts"].cpu().numpy()) == counts
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"rows H={H} variant {variant}")
+
+
 @pytest.mark.parametrize("E,K", [(1, 1), (6, 6), (6, 1), (130, 7), (256, 64)])
 def test_expert_counts(E, K):
     cfg = synth.MoeConfig(name="ek", cid=205, T=150, H=64, I=96, E=E, K=K)
