@@ -593,11 +593,21 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
         dma16(p, st + i * TL::NWAVES * 1024);
     };
     auto issue_b_nb = [&](int kt, int i) {
-        const uint32_t st = wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
         const uint32_t kc = (uint32_t)(kbeg + min(kt, nk - 1));
-        const uint8_t *p = b_src[i] + (uint64_t)kc * (2 * TL::BK);
-        if (RAGGED) p = ((int)kc * TL::BK + b_k[i] < Kd) ? p : zero;
-        dma16(p, st + i * TL::NWAVES * 1024);
+        if constexpr (TL::MX) {
+            // packed codes are zero past K; load NBC is the scale piece
+            if (i < TL::NBC) {
+                dma16(b_src[i] + (int64_t)kc * 1024,
+                      wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES + i * TL::NWAVES * 1024);
+            } else if (lane < 4 * TL::RBW) {
+                dma16(s_src + (int64_t)kc * 64, wave_sc + (kt % TL::SB) * TL::B_BYTES);
+            }
+        } else {
+            const uint32_t st = wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
+            const uint8_t *p = b_src[i] + (uint64_t)kc * (2 * TL::BK);
+            if (RAGGED) p = ((int)kc * TL::BK + b_k[i] < Kd) ? p : zero;
+            dma16(p, st + i * TL::NWAVES * 1024);
+        }
     };
     auto issue_a = [&](int kt) {
 #pragma unroll
@@ -752,8 +762,9 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
             }
         }
     };
-    // One wave per SIMD: the wave itself keeps the matrix pipe fed, so its
-    // instruction stream is laid out by hand (each sched_barrier fences the
+    // The hand-laid k-loop (the 4-wave 16-bit tile, where one wave per SIMD
+    // must keep the matrix pipe fed by itself, and the MXFP4 tiles, whose
+    // decode work then sits between the MFMAs; each sched_barrier fences the
     // compiler's scheduler).  In sub-steps 0 .. NKS-2 every MFMA is followed
     // by one item: a fragment read of the next sub-step, then a DMA load of
     // the step's group (A(kt+1), then B(kt+SB-1)), so the whole group goes
@@ -763,22 +774,35 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     auto kloop_il = [&](auto mv_tag) {
         constexpr int MV = decltype(mv_tag)::value;
         u32x4 bf[2][TL::FN], af[2][TL::FM > 0 ? TL::FM : 1];
+        u32x4 cq[TL::MX ? TL::FN : 1];     // MXFP4 codes of the current k-step
+        float scf[TL::MX ? TL::FN : 1];    // and their scale multipliers
         auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
         // fragment r of sub-step (kt, ks) into buffer b: weights r < FN,
-        // then tokens FN + m
+        // then tokens FN + m.  MXFP4: the k-step's codes and scale are read
+        // with sub-step 0, every sub-step decodes its 8 values per lane.
         auto read_one = [&](int kt, int ks, int b, int r) {
             const uint8_t *sa = lds + (kt % TL::SA) * TL::A_BYTES;
             const uint8_t *sb = lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
             const int coff = ((ks * 2 + lhalf) ^ lsw) * 16;
             if (r < TL::FN) {
-                bf[b][r] = *(const u32x4 *)(sb + (brow(r) + lrow) * TL::ROWB + coff);
-                if (F16) {
+                if constexpr (TL::MX) {
+                    if (ks == 0) {
+                        const int t = brow(r) / 32;
+                        cq[r] = *(const u32x4 *)(sb + t * 1024 + mx_code);
+                        scf[r] = e8m0_scale(sb[TL::CODE_BYTES + t * 64 + mx_scale]);
+                    }
+                    bf[b][r] = decode_mxfp4_8<F16>(cq[r][ks], scf[r]);
+                } else {
+                    bf[b][r] = *(const u32x4 *)(sb + (brow(r) + lrow) * TL::ROWB + coff);
+                    if (F16) {
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) bf[b][r][w] = bf16x2_to_f16x2(bf[b][r][w]);
+                        for (int w = 0; w < 4; ++w) bf[b][r][w] = bf16x2_to_f16x2(bf[b][r][w]);
+                    }
                 }
             } else {
                 const int m = r - TL::FN;
-                af[b][m] = *(const u32x4 *)(sa + (wm * TL::TM + m * 32 + lrow) * TL::ROWB + coff);
+                const int acoff = ((TL::MX ? 4 * lhalf + ks : ks * 2 + lhalf) ^ lsw) * 16;
+                af[b][m] = *(const u32x4 *)(sa + (wm * TL::TM + m * 32 + lrow) * TL::ROWB + acoff);
                 if (HIN && !F16 && hf[(kx(kt) * TL::BK) / g.h_width] == kHF16) {
 #pragma unroll
                     for (int w = 0; w < 4; ++w) af[b][m][w] = f16x2_to_bf16x2(af[b][m][w]);
@@ -845,8 +869,8 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     };
     // every wave runs the same loads and barriers; only its MFMA work differs
     const int mv = min(max((tw.nrows - wm * TL::TM + 31) / 32, 0), TL::FM);
-    if constexpr (TL::WPE == 1) {
-        static_assert(!TL::MX && TL::SB >= 3 && NKS >= 2, "interleaved loop: 16-bit weights");
+    if constexpr (TL::WPE == 1 || TL::MX) {
+        static_assert(TL::SB >= 3 && NKS >= 2, "interleaved loop");
         // every count of 32-row blocks up to FM has its own loop
         static_assert(TL::FM <= 8, "block counts");
         switch (mv) {
