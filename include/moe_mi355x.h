@@ -120,6 +120,15 @@ typedef struct moe_options {
                                      expert's weight scales the input it reads and
                                      its output joins the sum unweighted.  0 or 1;
                                      default 0                                      */
+    int32_t down_fp16_copy;       /* bf16 layers whose down weights convert exactly
+                                     to fp16 (checked by moe_prepare): 1 keeps a
+                                     library-owned fp16 copy of them (E*H*I*2 bytes
+                                     of device memory, made by moe_prepare, freed by
+                                     moe_destroy), so the fp16 down GEMM streams it
+                                     instead of converting each tile's weights in
+                                     registers.  If the allocation fails the layer
+                                     converts per tile instead, without error.
+                                     0 or 1; default 1                              */
 } moe_options;
 
 /* A device tensor view.  ndim == 0 (or data == NULL) marks an absent tensor.

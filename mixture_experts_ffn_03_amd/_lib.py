@@ -41,7 +41,7 @@ class moe_options(C.Structure):
                 ("swiglu_fusion", C.c_int32), ("swiglu_alpha", C.c_float),
                 ("swiglu_beta", C.c_float), ("swiglu_limit", C.c_float),
                 ("gemm_variant", C.c_int32), ("gelu_mode", C.c_int32),
-                ("weigh_inputs", C.c_int32)]
+                ("weigh_inputs", C.c_int32), ("down_fp16_copy", C.c_int32)]
 
 
 class moe_tensor(C.Structure):
@@ -121,7 +121,7 @@ def options(**kw) -> moe_options:
     (scoring/routing_mode, renormalize, n_group, topk_group,
     routed_scaling_factor, activation, swiglu_fusion, swiglu_alpha,
     swiglu_beta, swiglu_limit, gemm_variant, gelu_mode,
-    weigh_inputs / apply_router_weight_on_input)."""
+    weigh_inputs / apply_router_weight_on_input, down_fp16_copy)."""
     o = moe_options()
     check(lib().moe_options_default(C.byref(o)))
     for k, v in kw.items():

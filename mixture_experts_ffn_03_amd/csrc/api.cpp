@@ -37,6 +37,11 @@ struct moe_layer {
     // the bound router transposed to [E, H] (rows K-contiguous, like the
     // expert stacks) for the router GEMM; made at prepare, freed by destroy
     mutable void *wr_t = nullptr;
+    // options.down_fp16_copy: the bf16 down weights as fp16 [E, H, I],
+    // allocated at the first prepare that needs it, refilled by later ones;
+    // down_f16_ready says whether the current binding's copy is in it
+    mutable void *down_f16 = nullptr;
+    mutable bool down_f16_ready = false;
 };
 
 namespace {
@@ -527,6 +532,23 @@ moe_status prepare_locked(const moe_layer *l, hipStream_t s)
         if ((st = hip_check(e, "prepare weight scan"))) return st;
         ok = mx ? (r[1] >= 104u && r[2] <= 140u) : (r[0] <= 0x477fu);
     }
+    l->down_f16_ready = false;
+    if (ok && l->wdtype == MOE_DTYPE_BF16 && l->opts.down_fp16_copy) {
+        const int64_t elems = l->E * l->H * l->I;
+        if (!l->down_f16 && hipMalloc(&l->down_f16, (size_t)elems * 2) != hipSuccess) {
+            (void)hipGetLastError();   // no room: the down GEMM converts per tile
+            l->down_f16 = nullptr;
+        }
+        if (l->down_f16) {
+            // complete before prepare returns, like the rest of it (a forward on
+            // another stream may follow)
+            moe_status st = hip_check(launch_to_f16(l->w.down_experts.data, l->down_f16, elems, s),
+                                      "down weights to fp16");
+            if (!st) st = hip_check(hipStreamSynchronize(s), "prepare sync");
+            if (st) return st;
+            l->down_f16_ready = true;
+        }
+    }
     if (l->wdtype == MOE_DTYPE_F32 && has_router(l)) {
         // (the 16-bit path synchronised in its weight scan)
         moe_status st = hip_check(hipStreamSynchronize(s), "prepare sync");
@@ -556,6 +578,7 @@ moe_status moe_options_default(moe_options *o)
     o->swiglu_beta = 0.0f;
     o->swiglu_limit = 0.0f;
     o->gemm_variant = 0;
+    o->down_fp16_copy = 1;
     return MOE_OK;
 }
 
@@ -603,6 +626,8 @@ moe_status moe_create(int64_t E, int64_t H, int64_t I, int64_t K, moe_dtype wdty
         return fail(MOE_ERR_INVALID_ARGUMENT, "unknown gelu_mode %d", o.gelu_mode);
     if (o.weigh_inputs != 0 && o.weigh_inputs != 1)
         return fail(MOE_ERR_INVALID_ARGUMENT, "weigh_inputs must be 0 or 1");
+    if (o.down_fp16_copy != 0 && o.down_fp16_copy != 1)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "down_fp16_copy must be 0 or 1");
     if (o.swiglu_fusion < MOE_FUSION_NONE || o.swiglu_fusion > MOE_FUSION_SPLIT)
         return fail(MOE_ERR_INVALID_ARGUMENT, "unknown swiglu_fusion %d", o.swiglu_fusion);
     if (o.gemm_variant < 0 || o.gemm_variant > 3)
@@ -882,6 +907,7 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     g2.w.row_mul = 1;
     if (present(l->w.down_bias)) g2.w.b_gate = l->w.down_bias.data;
     g2.hfmt = g1.hfmt;
+    if (l->down_f16_ready && path != Path::kF32) g2.w_f16 = l->down_f16;
     g2.h_tiles = g1.nN;
     g2.h_width = bn1;
     g2.f16_ok = g1.f16_ok;
@@ -965,6 +991,7 @@ moe_status moe_destroy(moe_layer *l)
 {
     if (l && l->mx_pack) (void)hipFree(l->mx_pack);
     if (l && l->wr_t) (void)hipFree(l->wr_t);
+    if (l && l->down_f16) (void)hipFree(l->down_f16);
     delete l;
     return MOE_OK;
 }

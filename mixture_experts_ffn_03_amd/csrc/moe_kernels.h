@@ -93,6 +93,7 @@ struct GemmArgs {
     // h storage formats, one byte per (GEMM-1 M-tile, GEMM-1 feature tile):
     // written by the gated GEMM, read per reduction step by the down GEMM.
     uint8_t *hfmt;
+    const void *w_f16;           // down GEMM: the prepared fp16 copy of w_gate, or null
     int h_tiles;                 // GEMM-1 feature tiles (row stride of hfmt)
     int h_width;                 // h columns per GEMM-1 feature tile
     int f16_ok;                  // the down weights convert exactly to fp16
@@ -137,6 +138,10 @@ inline int64_t mx_pack_scale_bytes(int ops, int64_t Nh, int64_t K, int64_t E)
 {
     return E * (ops * Nh / 32) * ((K + 63) / 64) * 64;
 }
+
+// Prepare-time copy of a bf16 stack as fp16 (n elements; exact when the
+// stack passed the fp16 range scan).
+hipError_t launch_to_f16(const void *src, void *dst, int64_t n, hipStream_t s);
 
 // Range of a down-weight stack, for the choice of the fp16 down GEMM:
 // out[0] = max over elements of the bf16 magnitude bits (0x7f80 = inf),

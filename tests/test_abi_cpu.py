@@ -52,6 +52,7 @@ def test_options_default(L):
     assert o.routed_scaling_factor == 1.0
     assert (o.activation, o.swiglu_fusion) == (0, 2)
     assert (o.swiglu_alpha, o.swiglu_beta, o.swiglu_limit) == (1.0, 0.0, 0.0)
+    assert (o.gemm_variant, o.gelu_mode, o.weigh_inputs, o.down_fp16_copy) == (0, 0, 0, 1)
 
 
 def create(L, E=8, H=64, I=32, K=2, dtype="bf16", gub=False, db=False, **opt):
@@ -68,7 +69,7 @@ def create(L, E=8, H=64, I=32, K=2, dtype="bf16", gub=False, db=False, **opt):
     dict(n_group=4, topk_group=5), dict(n_group=4, topk_group=1, K=3),
     dict(n_group=128, E=256, topk_group=1, K=1), dict(scoring=7),
     dict(activation=6), dict(swiglu_fusion=3), dict(gemm_variant=4),
-    dict(gemm_variant=-1), dict(gelu_mode=2), dict(weigh_inputs=2)])
+    dict(gemm_variant=-1), dict(gelu_mode=2), dict(weigh_inputs=2), dict(down_fp16_copy=2)])
 def test_create_rejects_bad_geometry(L, kw):
     st, h = create(L, **kw)
     assert st == 1, L.lib().moe_last_error()

@@ -176,6 +176,17 @@ def test_tile_row_splits(H, variant):
     compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"rows H={H} variant {variant}")
 
 
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_down_weights_converted_per_tile(variant):
+    """down_fp16_copy = 0: the fp16 down GEMM converts its bf16 weight
+    fragments in registers (the default streams the prepared fp16 copy)."""
+    cfg = synth.MIXTRAL_SMALL
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, _ = run_gpu(cfg, inp, gemm_variant=variant, down_fp16_copy=0)
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"no fp16 copy variant {variant}")
+
+
 @pytest.mark.parametrize("E,K", [(1, 1), (6, 6), (6, 1), (130, 7), (256, 64)])
 def test_expert_counts(E, K):
     cfg = synth.MoeConfig(name="ek", cid=205, T=150, H=64, I=96, E=E, K=K)
