@@ -120,8 +120,9 @@ typedef struct moe_options {
                                      expert's weight scales the input it reads and
                                      its output joins the sum unweighted.  0 or 1;
                                      default 0                                      */
-    int32_t down_fp16_copy;       /* bf16 layers whose down weights convert exactly
-                                     to fp16 (checked by moe_prepare): 1 keeps a
+    int32_t down_fp16_copy;       /* bf16 layers whose down weights lie in fp16's
+                                     range (checked by moe_prepare; the fp16 down
+                                     GEMM runs only then): 1 keeps a
                                      library-owned fp16 copy of them (E*H*I*2 bytes
                                      of device memory, made by moe_prepare, freed by
                                      moe_destroy), so the fp16 down GEMM streams it

@@ -974,7 +974,8 @@ hipError_t launch_epi(int epi, const GemmArgs &a, int64_t max_m_tiles, hipStream
 }
 
 // ---- prepare-time fp16 copy of a bf16 stack (round to nearest even; exact
-// for the stacks the range scan passes)
+// for the stacks the range scan passes, save values below 2^-17, which keep
+// fewer bits as fp16 subnormals)
 __global__ __launch_bounds__(256) void to_f16_kernel(const uint16_t *src, _Float16 *dst, int64_t n)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;

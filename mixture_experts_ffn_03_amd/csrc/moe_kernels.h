@@ -139,8 +139,8 @@ inline int64_t mx_pack_scale_bytes(int ops, int64_t Nh, int64_t K, int64_t E)
     return E * (ops * Nh / 32) * ((K + 63) / 64) * 64;
 }
 
-// Prepare-time copy of a bf16 stack as fp16 (n elements; exact when the
-// stack passed the fp16 range scan).
+// Prepare-time copy of a bf16 stack as fp16 (n elements; the stack passed
+// the fp16 range scan).
 hipError_t launch_to_f16(const void *src, void *dst, int64_t n, hipStream_t s);
 
 // Range of a down-weight stack, for the choice of the fp16 down GEMM:
