@@ -153,7 +153,7 @@ size_t align256(size_t v)
 struct Workspace {
     size_t ids, weights, block_counts, block_base, counts, offsets, tile_cum1, tile_cum2,
         full_cum1, full_cum2,
-        row_token, slot_row, row_weight, logits, router_grp, hfmt, h, y, total;
+        row_token, slot_row, row_weight, logits, router_grp, hfmt, h, y, yfmt, total;
 };
 
 int64_t max_m_tiles_of(const moe_layer *l, int64_t T, int bm)
@@ -271,6 +271,8 @@ Workspace layout(const moe_layer *l, int64_t T)
     w.h = take(TK * l->I * hbytes);
     // y: one [T*K, H] f32 buffer per split of the down GEMM
     w.y = take(TK * l->H * 4 * down_splits(l, T, choose_path(l, T)));
+    // one y-format byte per (row, feature chunk) when y may be stored in fp16
+    w.yfmt = take(TK * ((l->H + kYWidth - 1) / kYWidth));
     w.total = o;
     return w;
 }
@@ -911,6 +913,12 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     g2.h_tiles = g1.nN;
     g2.h_width = bn1;
     g2.f16_ok = g1.f16_ok;
+    // a 16-bit layer without splits stores in-range y chunks in fp16: they are
+    // summed into a bf16 output whose rounding is 8x coarser than fp16's
+    if (path != Path::kF32 && splits == 1 && x->dtype == MOE_DTYPE_BF16) {
+        g2.yfmt = (uint8_t *)(wsb + W.yfmt);
+        g2.yfmt_stride = (l->H + kYWidth - 1) / kYWidth;
+    }
     if (mx) {
         g1.pk = l->mx_pack + l->mx_off[0];
         g1.pks = l->mx_pack + l->mx_off[1];
@@ -954,6 +962,8 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     ca.unit_weights = l->opts.weigh_inputs;
     ca.splits = splits;
     ca.split_stride = g2.split_stride;
+    ca.yfmt = g2.yfmt;
+    ca.yfmt_stride = g2.yfmt_stride;
     if ((st = hip_check(launch_combine(ca, s), "combine launch"))) return st;
     if ((st = mark(5))) return st;
     return copy_routing(l, T, wsb, W, routing, s);

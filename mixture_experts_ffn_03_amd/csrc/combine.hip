@@ -7,45 +7,102 @@
 // out[t, :] = sum_{j=0..K-1} w[t, j] * y[slot_row[t, j], :]  (+ shared[t, :])
 // accumulated in f32 in slot order j = 0, 1, ..., rounded once to the output
 // dtype (round to nearest even for bf16).  No atomics: each output element
-// is produced by one thread, so results are bitwise reproducible.
+// is produced by one thread, so results are bitwise reproducible.  A chunk
+// of y the down GEMM stored in fp16 (its format byte says so) is read as
+// fp16 and widened exactly.
 #include "moe_kernels.h"
 
 namespace moe {
 namespace {
 
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
+// Each thread produces 8 consecutive features of one token (one 16-byte bf16
+// store).  Slots are taken in groups of up to 8: their rows and weights
+// first, then, with chunk formats, each slot's format byte together with its
+// 16-byte fp16 load (both depend only on the row), so a group costs two
+// dependent memory round trips; an f32 chunk is loaded after its format is known.
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
 {
-    const int H4 = a.H / 4;
+    const int H8 = a.H / 8;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (int64_t)a.T * H4) return;
-    const int t = (int)(idx / H4), c = (int)(idx % H4) * 4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < a.K; ++j) {
-        const float w = a.unit_weights ? 1.0f : a.weights[(int64_t)t * a.K + j];
-        const int row = a.slot_row[(int64_t)t * a.K + j];
-        // the partial sums of a split down GEMM, added in split order
-        f32x4 v = *(const f32x4 *)(a.y + (int64_t)row * a.H + c);
-        for (int s = 1; s < a.splits; ++s)
-            v += *(const f32x4 *)(a.y + s * a.split_stride + (int64_t)row * a.H + c);
-        acc += w * v;
+    if (idx >= (int64_t)a.T * H8) return;
+    const int t = (int)(idx / H8), c = (int)(idx % H8) * 8;
+    const int q = c / kYWidth, q0 = q * kYWidth;
+    const int32_t *srow = a.slot_row + (int64_t)t * a.K;
+    const float *wrow = a.weights + (int64_t)t * a.K;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < a.K; j0 += 8) {
+        const int n = a.K - j0 < 8 ? a.K - j0 : 8;
+        // branch-free loads: slots past the group's end repeat its last one
+        // (and are not summed)
+        int row[8];
+        float w[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int j = j0 + (jj < n ? jj : n - 1);
+            row[jj] = srow[j];
+            w[jj] = wrow[j];
+        }
+        uint8_t fmt[8];
+        f16x8 h[8];
+        if (a.yfmt) {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const float *yr = a.y + (int64_t)row[jj] * a.H;
+                fmt[jj] = a.yfmt[(int64_t)row[jj] * a.yfmt_stride + q];
+                h[jj] = *(const f16x8 *)((const _Float16 *)(yr + q0) + (c - q0));
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            if (jj >= n) break;
+            float v[8];
+            if (a.yfmt && fmt[jj] == kYF16) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (float)h[jj][e];
+            } else {
+                // f32 chunk; or the partial sums of a split down GEMM, added
+                // in split order
+                const float *yr = a.y + (int64_t)row[jj] * a.H + c;
+                f32x4 lo = *(const f32x4 *)yr, hi = *(const f32x4 *)(yr + 4);
+                for (int s = 1; s < a.splits; ++s) {
+                    lo += *(const f32x4 *)(yr + s * a.split_stride);
+                    hi += *(const f32x4 *)(yr + s * a.split_stride + 4);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = lo[e];
+                    v[e + 4] = hi[e];
+                }
+            }
+            const float wj = a.unit_weights ? 1.0f : w[jj];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += wj * v[e];
+        }
     }
     const int64_t o = (int64_t)t * a.H + c;
     if (a.out_bf16) {
         if (a.shared) {
-            const bf16x4 s = *(const bf16x4 *)((const __bf16 *)a.shared + o);
+            const bf16x8 sh = *(const bf16x8 *)((const __bf16 *)a.shared + o);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] += (float)s[j];
+            for (int e = 0; e < 8; ++e) acc[e] += (float)sh[e];
         }
-        bf16x4 r;
+        bf16x8 r;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = (__bf16)acc[j];
-        *(bf16x4 *)((__bf16 *)a.out + o) = r;
+        for (int e = 0; e < 8; ++e) r[e] = (__bf16)acc[e];
+        *(bf16x8 *)((__bf16 *)a.out + o) = r;
     } else {
-        if (a.shared) acc += *(const f32x4 *)((const float *)a.shared + o);
-        *(f32x4 *)((float *)a.out + o) = acc;
+        float *out = (float *)a.out + o;
+        if (a.shared) {
+            const float *sh = (const float *)a.shared + o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += sh[e];
+        }
+        *(f32x4 *)out = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        *(f32x4 *)(out + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
     }
 }
 
@@ -53,7 +110,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
 {
-    const int64_t n = (int64_t)a.T * (a.H / 4);
+    // one thread per 8 features of a token (H is a multiple of 8)
+    const int64_t n = (int64_t)a.T * (a.H / 8);
     const int64_t blocks = (n + 255) / 256;
     combine_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
     return hipGetLastError();

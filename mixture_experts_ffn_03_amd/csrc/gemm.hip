@@ -19,8 +19,11 @@
 //         normal case), a workgroup converts the bf16 (or MXFP4) down weights
 //         exactly to fp16 after their LDS read and runs the f16 MFMA;
 //         otherwise it rounds the fp16 h fragments to bf16 and runs the bf16
-//         MFMA.  Adds the down bias and stores y in f32; the combine rounds
-//         once, after the weighted sum.
+//         MFMA.  Adds the down bias and stores y per 64-feature chunk of a
+//         row: fp16 when the chunk fits fp16's range (half the bytes the
+//         combine reads back), else f32, with one format byte per chunk; a
+//         split reduction stores f32 partial sums.  The combine rounds to the
+//         output dtype once, after the weighted sum.
 //
 // The token operand of the gated GEMM is gathered straight from x through the
 // permutation (row_token), so the permuted activations are never written.
@@ -313,6 +316,78 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
         float *y = (float *)g.out + (int64_t)tw.ks * g.split_stride;
         const void *bias = tw.ks == 0 ? g.w.b_gate : nullptr;
         const int64_t eb = (int64_t)tw.e * g.w.e_rows;
+        if constexpr (EPI == kEpiDown) {
+            // a wave's features of one row form one chunk, held by lanes l
+            // and l ^ 32: with yfmt, fp16 when its max |y| fits (every chunk is
+            // written, so the formats need no clearing); else (split partial
+            // sums, f32 layers) f32.  The bias, if any, is read once.  (One
+            // store path for both: two made the 4-wave tile spill.)
+            static_assert(TL::TN == kYWidth, "one y chunk per wave and row");
+            const int q0 = tw.n0 + wn * TL::TN;
+            auto chunks = [&](auto with_bias) {
+                constexpr bool B = decltype(with_bias)::value;
+                float bv[TL::FN][16];
+                if constexpr (B) {
+#pragma unroll
+                    for (int f = 0; f < TL::FN; ++f)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int c = q0 + f * 32 + (i / 4) * 8 + fq + i % 4;
+                            bv[f][i] = c < g.Nout ? bias_at(bias, eb + c) : 0.f;
+                        }
+                }
+                auto yval = [&](int f, int m, int i) {
+                    float a = acc[f][m][i];
+                    // the 4-wave tile's accumulators live in AGPRs: move each
+                    // where it is used (the compiler otherwise copies all
+                    // 256 to VGPRs after the k-loop, and spills)
+                    if constexpr (TL::WPE == 1)
+                        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a) : "a"(a));
+                    if constexpr (B) return a + bv[f][i];
+                    else return a;
+                };
+                if (q0 >= g.Nout) return;
+                // one pass per row block: its chunk max, then its stores
+#pragma unroll
+                for (int m = 0; m < TL::FM; ++m) {
+                    float v[TL::FN][16];
+                    float mx = 0.f;
+#pragma unroll
+                    for (int f = 0; f < TL::FN; ++f)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            v[f][i] = yval(f, m, i);
+                            if (q0 + f * 32 + (i / 4) * 8 + fq < g.Nout) mx = fmaxf(mx, fabsf(v[f][i]));
+                        }
+                    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                    const int tl = wm * TL::TM + m * 32 + lrow;
+                    if (tl >= tw.nrows) continue;
+                    const int64_t row = tw.row0 + tl;
+                    const bool h16 = g.yfmt && mx <= 65504.f;
+                    if (g.yfmt && fq == 0)
+                        g.yfmt[row * g.yfmt_stride + q0 / kYWidth] = h16 ? kYF16 : kYF32;
+                    float *yq = y + row * g.Nout + q0;
+#pragma unroll
+                    for (int f = 0; f < TL::FN; ++f)
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4) {
+                            const int cc = f * 32 + i4 * 8 + fq, r0 = i4 * 4;
+                            if (q0 + cc >= g.Nout) continue;
+                            if (h16) {
+                                f16x4 o = {(_Float16)v[f][r0], (_Float16)v[f][r0 + 1],
+                                           (_Float16)v[f][r0 + 2], (_Float16)v[f][r0 + 3]};
+                                *(f16x4 *)((_Float16 *)yq + cc) = o;
+                            } else {
+                                f32x4 o = {v[f][r0], v[f][r0 + 1], v[f][r0 + 2], v[f][r0 + 3]};
+                                *(f32x4 *)(yq + cc) = o;
+                            }
+                        }
+                }
+            };
+            if (bias) chunks(std::true_type{});
+            else chunks(std::false_type{});
+            return;
+        }
 #pragma unroll
         for (int f = 0; f < TL::FN; ++f)
 #pragma unroll
@@ -936,9 +1011,12 @@ __global__ __launch_bounds__(TL::NT, TL::WPE) void gemm_dma_kernel(GemmArgs g)
         if (f16 && !TL::MX && g.w_f16) {
             if (ragged) dma_body<TL, EPI, true, true, !TL::MX>(g, tw, lds, s_red);
             else dma_body<TL, EPI, true, false, !TL::MX>(g, tw, lds, s_red);
-        } else if (f16) {
-            if (ragged) dma_body<TL, EPI, true, true>(g, tw, lds, s_red);
-            else dma_body<TL, EPI, true, false>(g, tw, lds, s_red);
+        } else if (TL::WPE != 1 && f16) {
+            // (the one-wave-per-SIMD tile runs only with the prepared fp16 copy)
+            if constexpr (TL::WPE != 1) {
+                if (ragged) dma_body<TL, EPI, true, true>(g, tw, lds, s_red);
+                else dma_body<TL, EPI, true, false>(g, tw, lds, s_red);
+            }
         } else {
             if (ragged) dma_body<TL, EPI, false, true>(g, tw, lds, s_red);
             else dma_body<TL, EPI, false, false>(g, tw, lds, s_red);

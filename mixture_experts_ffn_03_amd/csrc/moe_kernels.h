@@ -62,6 +62,12 @@ struct WeightRows {
 // Storage format of one h tile (GEMM-1 output tile, read by the down GEMM).
 enum : uint8_t { kHF16 = 0, kHBF16 = 1 };
 
+// Storage format of one chunk of y: kYWidth consecutive features of one row.
+// An fp16 chunk (every value within fp16's range) occupies the first half of
+// the chunk's f32 space; the combine reads each chunk in its own format.
+enum : uint8_t { kYF32 = 0, kYF16 = 1 };
+constexpr int kYWidth = 64;
+
 // Epilogue (and operand) mode of a grouped GEMM launch.
 //  kEpiDown   down GEMM: A = h (16-bit, per-tile formats), y = acc + bias, f32
 //  kEpiGated  gate||up GEMM: gate/up row pairs, gated activation, 16-bit h
@@ -94,6 +100,10 @@ struct GemmArgs {
     // written by the gated GEMM, read per reduction step by the down GEMM.
     uint8_t *hfmt;
     const void *w_f16;           // down GEMM: the prepared fp16 copy of w_gate, or null
+    // down GEMM without splits, or null (y in f32): per-chunk storage format
+    // of y, one byte per (row r, kYWidth-feature chunk q) at yfmt[r * yfmt_stride + q]
+    uint8_t *yfmt;
+    int64_t yfmt_stride;
     int h_tiles;                 // GEMM-1 feature tiles (row stride of hfmt)
     int h_width;                 // h columns per GEMM-1 feature tile
     int f16_ok;                  // the down weights convert exactly to fp16
@@ -160,6 +170,8 @@ struct CombineArgs {
     int unit_weights;            // weigh-inputs: every kept output weighs 1
     int splits;                  // y holds this many partial sums (split reduction),
     int64_t split_stride;        // split_stride elements apart, summed in order
+    const uint8_t *yfmt;         // splits == 1: y chunk formats (GemmArgs yfmt), or null
+    int64_t yfmt_stride;
 };
 
 // Dense f32 grouped GEMM (the fp32 layer): same contract as GemmArgs with
