@@ -133,8 +133,140 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
     const int wn = wave % TL::WN, wm = wave / TL::WN;
     const int lrow = lane & 31;
     const int fq = (lane >> 5) * 4;
-    if constexpr (EPI == kEpiGated || EPI == kEpiAct) {
-        // features of the h tile held per wave: gate/up pairs, or every block
+    // accumulator (f, m) element i; the 4-wave tile's accumulators live in
+    // AGPRs and are moved out one by one where they are used (otherwise the
+    // compiler copies all 256 to VGPRs after the k-loop, and spills)
+    auto accv = [&](int f, int m, int i) {
+        float a = acc[f][m][i];
+        if constexpr (TL::WPE == 1) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a) : "a"(a));
+        return a;
+    };
+    if constexpr (EPI == kEpiAct) {
+        // fc1 of a non-gated expert: h = act(rs * acc + b), rs the row's
+        // weight under weigh-inputs routing.  Pass 1 takes the tile's max |h|
+        // without keeping h; pass 2 recomputes h at the store (keeping every
+        // activated accumulator live across the block max spilled thousands
+        // of registers).  The activation is uniform: one unrolled body each.
+        const int64_t eb = (int64_t)tw.e * g.w.e_rows;
+        const int cw = tw.n0 + wn * TL::TN;           // first feature of this wave
+        float rs[TL::FM];
+        bool tok_ok[TL::FM];
+#pragma unroll
+        for (int m = 0; m < TL::FM; ++m) {
+            const int tl = wm * TL::TM + m * 32 + lrow;
+            tok_ok[m] = tl < tw.nrows;
+            rs[m] = (g.row_w && tok_ok[m]) ? g.row_w[tw.row0 + tl] : 1.0f;
+        }
+        // bias of each held feature (a column past Nout reads the last
+        // one's): read once into registers on the 4-wave tile, whose
+        // accumulators sit in AGPRs; at each use (an L1 hit) on the others,
+        // where registers are the scarcer
+        const uint16_t *bp = (const uint16_t *)g.w.b_gate;
+        auto bias_of = [&](int f, int i) {
+            const int c = min(cw + f * 32 + (i / 4) * 8 + fq + i % 4, g.Nout - 1);
+            return bp ? bf16_bits_to_float(bp[eb + (int64_t)c * g.w.row_mul + g.w.off_gate]) : 0.0f;
+        };
+        float bv[TL::FN][16];
+        if constexpr (TL::WPE == 1) {
+#pragma unroll
+            for (int f = 0; f < TL::FN; ++f)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) bv[f][i] = bias_of(f, i);
+        }
+        constexpr int PITCH = TL::BN * 2 + 16;
+        constexpr bool STAGED = 256 + TL::BM * PITCH <= TL::LDS_BYTES;
+        uint16_t *h = (uint16_t *)g.out;
+        auto finish = [&](auto act) {
+            auto hval = [&](int f, int m, int i) {
+                float b;
+                if constexpr (TL::WPE == 1) b = bv[f][i];
+                else b = bias_of(f, i);
+                return act(accv(f, m, i) * rs[m] + b);
+            };
+            float hm = 0.0f;
+#pragma unroll
+            for (int f = 0; f < TL::FN; ++f)
+#pragma unroll
+                for (int m = 0; m < TL::FM; ++m)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const bool ok = tok_ok[m] && cw + f * 32 + (i / 4) * 8 + fq + i % 4 < g.Nout;
+                        const float v = hval(f, m, i);
+                        hm = fmaxf(hm, ok ? fabsf(v) : 0.0f);
+                    }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) hm = fmaxf(hm, __shfl_xor(hm, off, 64));
+            if (lane == 0) s_red[wave] = hm;
+            __syncthreads();
+            float bmax = s_red[0];
+#pragma unroll
+            for (int w = 1; w < NWAVES; ++w) bmax = fmaxf(bmax, s_red[w]);
+            const bool f16 = g.f16_ok && bmax <= 65504.0f;
+            if (tid == 0) g.hfmt[(int64_t)tw.mg * g.h_tiles + tw.nt] = f16 ? kHF16 : kHBF16;
+            // pass 2: 4 features of a token per lane, through LDS when the
+            // tile fits (whole 16-byte row chunks out), else straight to h
+            auto put = [&](int f, int m, int i4, uint16_t *dst) {
+                const int r0 = i4 * 4;
+                if (f16) {
+                    f16x4 o = {(_Float16)hval(f, m, r0), (_Float16)hval(f, m, r0 + 1),
+                               (_Float16)hval(f, m, r0 + 2), (_Float16)hval(f, m, r0 + 3)};
+                    *(f16x4 *)dst = o;
+                } else {
+                    bf16x4 o = {(__bf16)hval(f, m, r0), (__bf16)hval(f, m, r0 + 1),
+                                (__bf16)hval(f, m, r0 + 2), (__bf16)hval(f, m, r0 + 3)};
+                    *(bf16x4 *)dst = o;
+                }
+            };
+            if constexpr (STAGED) {
+                uint8_t *hs = lds + 256;
+                __syncthreads();                 // every wave has read s_red
+#pragma unroll
+                for (int f = 0; f < TL::FN; ++f)
+#pragma unroll
+                    for (int m = 0; m < TL::FM; ++m) {
+                        const int tl = wm * TL::TM + m * 32 + lrow;
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4) {
+                            const int cl = wn * TL::TN + f * 32 + i4 * 8 + fq;
+                            put(f, m, i4, (uint16_t *)(hs + tl * PITCH + cl * 2));
+                        }
+                    }
+                __syncthreads();
+                constexpr int CPRH = TL::BN / 8;
+                for (int q = tid; q < TL::BM * CPRH; q += TL::NT) {
+                    const int r = q / CPRH, ch = q % CPRH;
+                    const int c = tw.n0 + ch * 8;
+                    if (r < tw.nrows && c < g.Nout)
+                        *(u32x4 *)(h + (int64_t)(tw.row0 + r) * g.Nout + c) =
+                            *(const u32x4 *)(hs + r * PITCH + ch * 16);
+                }
+            } else {
+#pragma unroll
+                for (int f = 0; f < TL::FN; ++f)
+#pragma unroll
+                    for (int m = 0; m < TL::FM; ++m) {
+                        if (!tok_ok[m]) continue;
+                        const int tl = wm * TL::TM + m * 32 + lrow;
+                        uint16_t *hrow = h + (int64_t)(tw.row0 + tl) * g.Nout;
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4) {
+                            const int c = cw + f * 32 + i4 * 8 + fq;
+                            if (c < g.Nout) put(f, m, i4, hrow + c);
+                        }
+                    }
+            }
+        };
+        switch (g.act) {
+        case 2: finish([](float x) { return fmaxf(x, 0.0f); }); break;
+        case 3:
+            if (g.gelu_mode == 1) finish([](float x) { return gelu_tanh_fast(x); });
+            else finish([](float x) { return gelu_erf_fast(x); });
+            break;
+        case 4: finish([](float x) { return x * sigmoid_fast(x); }); break;
+        default: finish([](float x) { return x; });
+        }
+    } else if constexpr (EPI == kEpiGated) {
+        // features of the h tile held per wave: gate/up pairs
         constexpr int FH = GATED ? TL::FN / 2 : TL::FN;
         constexpr int WH = GATED ? TL::TN / 2 : TL::TN;
         // pass 1: activation into the (gate) accumulators, tile max |h|.
@@ -193,10 +325,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
         };
         const bool bias = bgs != 0 || bus != 0;
         auto run = [&](auto act) {
-            if constexpr (GATED)
-                return bias ? pass1(std::true_type{}, act) : pass1(std::false_type{}, act);
-            else
-                return pass1(std::true_type{}, act);
+            return bias ? pass1(std::true_type{}, act) : pass1(std::false_type{}, act);
         };
         float hmax;
         if constexpr (GATED) {
@@ -212,22 +341,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
                     });
                 else
                     hmax = run([=](float x, float u) { return x * sigmoid_fast(al * x) * (u + be); });
-            }
-        } else {
-            switch (g.act) {
-            case 2: hmax = run([](float x, float) { return fmaxf(x, 0.0f); }); break;
-            case 3:
-                if (g.gelu_mode == 1)
-                    hmax = run([](float x, float) {
-                        return 0.5f * x * (1.0f + tanhf(0.7978845608f * (x + 0.044715f * x * x * x)));
-                    });
-                else
-                    hmax = run([](float x, float) {
-                        return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
-                    });
-                break;
-            case 4: hmax = run([](float x, float) { return x * sigmoid_fast(x); }); break;
-            default: hmax = run([](float x, float) { return x; });
             }
         }
         // block max -> storage format of this h tile

@@ -107,6 +107,30 @@ __device__ inline float sigmoid_fast(float v)
     return __builtin_amdgcn_rcpf(1.0f + __expf(-v));
 }
 
+// GELU for the 16-bit GEMM-1 epilogue, where h is stored in 16 bits, in
+// branch-free forms (inlined per accumulator, the library erff / tanhf made
+// the fully unrolled epilogue spill thousands of registers).
+// Erf form: x * Phi(x), with Phi taken from erfc(z), z = |x| / sqrt(2), by
+// the rational approximation of Abramowitz & Stegun, formula 7.1.26
+// (|error| <= 1.5e-7): erfc(z) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^(-z^2),
+// t = 1 / (1 + p z).  For x < 0, Phi(x) = erfc(z) / 2 directly, with no
+// cancellation; for x >= 0, Phi(x) = 1 - erfc(z) / 2.
+__device__ inline float gelu_erf_fast(float x)
+{
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * z);
+    const float p = t * (0.254829592f +
+                         t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+    const float ec = p * __expf(-z * z);
+    return x >= 0.0f ? x * (1.0f - 0.5f * ec) : 0.5f * x * ec;
+}
+
+// Tanh form: 0.5 x (1 + tanh(u)) = x * sigmoid(2u), u = sqrt(2/pi) (x + 0.044715 x^3).
+__device__ inline float gelu_tanh_fast(float x)
+{
+    return x * sigmoid_fast(1.5957691216057308f * (x + 0.044715f * x * x * x));
+}
+
 // Gated activation in fp32.  act 0: SiLU-gated, h = g*sigmoid(g)*u.
 // act 1: clamped SwiGLU, g' = min(g, L), u' = clamp(u, -L, L) when L > 0,
 // h = g'*sigmoid(alpha*g')*(u' + beta).
