@@ -60,7 +60,8 @@ class Hip:
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("gemm.hip", "gemm_common.h", "moe_kernels.h"):
+    for f in ("gemm.hip", "gemm_kernels.h", "gemm_prefill.hip", "gemm_prefill_mx.hip",
+              "gemm_mid.hip", "gemm_decode.hip", "gemm_common.h", "moe_kernels.h"):
         with open(os.path.join(ROOT, "mixture_experts_ffn_03_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -19,7 +19,10 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "gemm_f32.hip",
+# the grouped-GEMM tile families are separate translation units so that they
+# compile in parallel
+SOURCES = ["gemm_prefill.hip", "gemm_prefill_mx.hip", "gemm_mid.hip", "gemm_decode.hip",
+           "api.cpp", "route.hip", "permute.hip", "gemm.hip", "gemm_f32.hip",
            "combine.hip", "router.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
