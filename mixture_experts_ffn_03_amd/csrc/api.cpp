@@ -271,8 +271,8 @@ Workspace layout(const moe_layer *l, int64_t T)
     w.h = take(TK * l->I * hbytes);
     // y: one [T*K, H] f32 buffer per split of the down GEMM
     w.y = take(TK * l->H * 4 * down_splits(l, T, choose_path(l, T)));
-    // one y-format byte per (row, feature chunk) when y may be stored in fp16
-    w.yfmt = take(TK * ((l->H + kYWidth - 1) / kYWidth));
+    // one y-format byte per (split, row, feature chunk) when y may be stored in fp16
+    w.yfmt = take(TK * ((l->H + kYWidth - 1) / kYWidth) * down_splits(l, T, choose_path(l, T)));
     w.total = o;
     return w;
 }
@@ -886,7 +886,7 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
         if (present(l->w.gate_up_bias)) w1.b_up = l->w.gate_up_bias.data;
     }
 
-    // GEMM 2: down + bias -> y (f32)
+    // GEMM 2: down + bias -> y (f32 space; in-range chunks stored in fp16 when yfmt is set)
     GemmArgs g2{};
     g2.a = wsb + W.h;
     g2.row_token = nullptr;
@@ -913,11 +913,12 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     g2.h_tiles = g1.nN;
     g2.h_width = bn1;
     g2.f16_ok = g1.f16_ok;
-    // a 16-bit layer without splits stores in-range y chunks in fp16: they are
-    // summed into a bf16 output whose rounding is 8x coarser than fp16's
-    if (path != Path::kF32 && splits == 1 && x->dtype == MOE_DTYPE_BF16) {
+    // a 16-bit layer stores in-range y chunks (or partial-sum chunks) in fp16:
+    // they are summed into a bf16 output whose rounding is 8x coarser than fp16's
+    if (path != Path::kF32 && x->dtype == MOE_DTYPE_BF16) {
         g2.yfmt = (uint8_t *)(wsb + W.yfmt);
         g2.yfmt_stride = (l->H + kYWidth - 1) / kYWidth;
+        g2.yfmt_split_stride = T * l->K * g2.yfmt_stride;
     }
     if (mx) {
         g1.pk = l->mx_pack + l->mx_off[0];
@@ -964,6 +965,7 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     ca.split_stride = g2.split_stride;
     ca.yfmt = g2.yfmt;
     ca.yfmt_stride = g2.yfmt_stride;
+    ca.yfmt_split_stride = g2.yfmt_split_stride;
     if ((st = hip_check(launch_combine(ca, s), "combine launch"))) return st;
     if ((st = mark(5))) return st;
     return copy_routing(l, T, wsb, W, routing, s);

@@ -20,10 +20,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // Each thread produces 8 consecutive features of one token (one 16-byte bf16
-// store).  Slots are taken in groups of up to 8: their rows and weights
-// first, then, with chunk formats, each slot's format byte together with its
-// 16-byte fp16 load (both depend only on the row), so a group costs two
-// dependent memory round trips; an f32 chunk is loaded after its format is known.
+// store).  The (slot, split) pieces of y it sums are taken 8 at a time
+// (8 / splits slots per group): the slots' rows and weights first, then, with
+// chunk formats, each piece's format byte together with its 16-byte fp16 load
+// (both depend only on the row), so a group costs two dependent memory round
+// trips; an f32 piece is loaded once its format is known.  S = splits is a
+// template parameter so that every piece index is a compile-time constant.
+template <int S>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
 {
     const int H8 = a.H / 8;
@@ -33,49 +36,52 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     const int q = c / kYWidth, q0 = q * kYWidth;
     const int32_t *srow = a.slot_row + (int64_t)t * a.K;
     const float *wrow = a.weights + (int64_t)t * a.K;
+    constexpr int G = 8 / S;                 // slots per group
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < a.K; j0 += 8) {
-        const int n = a.K - j0 < 8 ? a.K - j0 : 8;
+    for (int j0 = 0; j0 < a.K; j0 += G) {
+        const int n = a.K - j0 < G ? a.K - j0 : G;
         // branch-free loads: slots past the group's end repeat its last one
         // (and are not summed)
-        int row[8];
-        float w[8];
+        int row[G];
+        float w[G];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
+        for (int jj = 0; jj < G; ++jj) {
             const int j = j0 + (jj < n ? jj : n - 1);
             row[jj] = srow[j];
             w[jj] = wrow[j];
         }
-        uint8_t fmt[8];
-        f16x8 h[8];
+        // piece p = (slot p / S, split p % S)
+        uint8_t fmt[G * S];
+        f16x8 h[G * S];
         if (a.yfmt) {
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const float *yr = a.y + (int64_t)row[jj] * a.H;
-                fmt[jj] = a.yfmt[(int64_t)row[jj] * a.yfmt_stride + q];
-                h[jj] = *(const f16x8 *)((const _Float16 *)(yr + q0) + (c - q0));
+            for (int p = 0; p < G * S; ++p) {
+                const int jj = p / S, sp = p % S;
+                const float *yr = a.y + sp * a.split_stride + (int64_t)row[jj] * a.H;
+                fmt[p] = a.yfmt[sp * a.yfmt_split_stride + (int64_t)row[jj] * a.yfmt_stride + q];
+                h[p] = *(const f16x8 *)((const _Float16 *)(yr + q0) + (c - q0));
             }
         }
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
+        for (int jj = 0; jj < G; ++jj) {
             if (jj >= n) break;
-            float v[8];
-            if (a.yfmt && fmt[jj] == kYF16) {
+            // the partial sums of a split down GEMM, added in split order,
+            // each chunk in its own format
+            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = (float)h[jj][e];
-            } else {
-                // f32 chunk; or the partial sums of a split down GEMM, added
-                // in split order
-                const float *yr = a.y + (int64_t)row[jj] * a.H + c;
-                f32x4 lo = *(const f32x4 *)yr, hi = *(const f32x4 *)(yr + 4);
-                for (int s = 1; s < a.splits; ++s) {
-                    lo += *(const f32x4 *)(yr + s * a.split_stride);
-                    hi += *(const f32x4 *)(yr + s * a.split_stride + 4);
-                }
+            for (int sp = 0; sp < S; ++sp) {
+                const int p = jj * S + sp;
+                if (a.yfmt && fmt[p] == kYF16) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[e] = lo[e];
-                    v[e + 4] = hi[e];
+                    for (int e = 0; e < 8; ++e) v[e] += (float)h[p][e];
+                } else {
+                    const float *yr = a.y + sp * a.split_stride + (int64_t)row[jj] * a.H + c;
+                    const f32x4 lo = *(const f32x4 *)yr, hi = *(const f32x4 *)(yr + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[e] += lo[e];
+                        v[e + 4] += hi[e];
+                    }
                 }
             }
             const float wj = a.unit_weights ? 1.0f : w[jj];
@@ -113,7 +119,13 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
     // one thread per 8 features of a token (H is a multiple of 8)
     const int64_t n = (int64_t)a.T * (a.H / 8);
     const int64_t blocks = (n + 255) / 256;
-    combine_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
+    switch (a.splits) {
+    case 1: combine_kernel<1><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a); break;
+    case 2: combine_kernel<2><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a); break;
+    case 3: combine_kernel<3><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a); break;
+    case 4: combine_kernel<4><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;    // the down GEMM splits at most 4 ways
+    }
     return hipGetLastError();
 }
 

@@ -19,10 +19,10 @@
 //         normal case), a workgroup converts the bf16 (or MXFP4) down weights
 //         exactly to fp16 after their LDS read and runs the f16 MFMA;
 //         otherwise it rounds the fp16 h fragments to bf16 and runs the bf16
-//         MFMA.  Adds the down bias and stores y per 64-feature chunk of a
-//         row: fp16 when the chunk fits fp16's range (half the bytes the
-//         combine reads back), else f32, with one format byte per chunk; a
-//         split reduction stores f32 partial sums.  The combine rounds to the
+//         MFMA.  Adds the down bias and stores y (or, with a split reduction,
+//         each split's partial sums) per 64-feature chunk of a row: fp16 when
+//         the chunk fits fp16's range (half the bytes the combine reads back),
+//         else f32, with one format byte per chunk.  The combine rounds to the
 //         output dtype once, after the weighted sum.
 //
 // The token operand of the gated GEMM is gathered straight from x through the
@@ -438,8 +438,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
         if constexpr (EPI == kEpiDown) {
             // a wave's features of one row form one chunk, held by lanes l
             // and l ^ 32: with yfmt, fp16 when its max |y| fits (every chunk is
-            // written, so the formats need no clearing); else (split partial
-            // sums, f32 layers) f32.  The bias, if any, is read once.  (One
+            // written, so the formats need no clearing); else (f32 layers) f32.  The bias, if any, is read once.  (One
             // store path for both: two made the 4-wave tile spill.)
             static_assert(TL::TN == kYWidth, "one y chunk per wave and row");
             const int q0 = tw.n0 + wn * TL::TN;
@@ -484,7 +483,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
                     const int64_t row = tw.row0 + tl;
                     const bool h16 = g.yfmt && mx <= 65504.f;
                     if (g.yfmt && fq == 0)
-                        g.yfmt[row * g.yfmt_stride + q0 / kYWidth] = h16 ? kYF16 : kYF32;
+                        g.yfmt[tw.ks * g.yfmt_split_stride + row * g.yfmt_stride + q0 / kYWidth] =
+                            h16 ? kYF16 : kYF32;
                     float *yq = y + row * g.Nout + q0;
 #pragma unroll
                     for (int f = 0; f < TL::FN; ++f)

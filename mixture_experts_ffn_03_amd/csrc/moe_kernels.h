@@ -69,7 +69,8 @@ enum : uint8_t { kYF32 = 0, kYF16 = 1 };
 constexpr int kYWidth = 64;
 
 // Epilogue (and operand) mode of a grouped GEMM launch.
-//  kEpiDown   down GEMM: A = h (16-bit, per-tile formats), y = acc + bias, f32
+//  kEpiDown   down GEMM: A = h (16-bit, per-tile formats), y = acc + bias, f32 or
+//             fp16 per 64-feature chunk (yfmt)
 //  kEpiGated  gate||up GEMM: gate/up row pairs, gated activation, 16-bit h
 //  kEpiAct    fc1 GEMM of a non-gated expert: activation of each row, 16-bit h
 //  kEpiPlain  A = x, y = acc + bias, f32 (the router GEMM, one group)
@@ -89,8 +90,8 @@ struct GemmArgs {
     int nN;                      // feature tiles
     int ksplit;                  // reduction splits (>= 1): split s reduces k-steps
                                  // [s*nk/ksplit, (s+1)*nk/ksplit) into out + s*split_stride
-    int64_t split_stride;        // elements between the splits' outputs (f32 y only)
-    void *out;                   // h bf16 [T*K, I] or y f32 [T*K, H]
+    int64_t split_stride;        // elements between the splits' outputs (f32 space)
+    void *out;                   // h 16-bit [T*K, I], or y [T*K, H] in f32 space (see yfmt)
     int act;                     // moe_activation code (0..5)
     int gelu_mode;               // 0 erf, 1 tanh
     float alpha, beta, limit;
@@ -100,10 +101,11 @@ struct GemmArgs {
     // written by the gated GEMM, read per reduction step by the down GEMM.
     uint8_t *hfmt;
     const void *w_f16;           // down GEMM: the prepared fp16 copy of w_gate, or null
-    // down GEMM without splits, or null (y in f32): per-chunk storage format
-    // of y, one byte per (row r, kYWidth-feature chunk q) at yfmt[r * yfmt_stride + q]
+    // down GEMM, or null (y in f32): per-chunk storage format of y (of each
+    // split's partial sums), one byte per (split s, row r, kYWidth-feature
+    // chunk q) at yfmt[s * yfmt_split_stride + r * yfmt_stride + q]
     uint8_t *yfmt;
-    int64_t yfmt_stride;
+    int64_t yfmt_stride, yfmt_split_stride;
     int h_tiles;                 // GEMM-1 feature tiles (row stride of hfmt)
     int h_width;                 // h columns per GEMM-1 feature tile
     int f16_ok;                  // the down weights convert exactly to fp16
@@ -170,8 +172,8 @@ struct CombineArgs {
     int unit_weights;            // weigh-inputs: every kept output weighs 1
     int splits;                  // y holds this many partial sums (split reduction),
     int64_t split_stride;        // split_stride elements apart, summed in order
-    const uint8_t *yfmt;         // splits == 1: y chunk formats (GemmArgs yfmt), or null
-    int64_t yfmt_stride;
+    const uint8_t *yfmt;         // y chunk formats (GemmArgs yfmt), or null
+    int64_t yfmt_stride, yfmt_split_stride;
 };
 
 // Dense f32 grouped GEMM (the fp32 layer): same contract as GemmArgs with

@@ -124,13 +124,17 @@ def test_h_overflow_falls_back_to_bf16(variant):
     compare_out(out, ref["out"], "bf16", f"h overflow variant {variant}")
 
 
+@pytest.mark.parametrize("I", [256, 2304])
 @pytest.mark.parametrize("variant", [1, 2])
-def test_y_chunks_beyond_fp16_stay_f32(variant):
+def test_y_chunks_beyond_fp16_stay_f32(variant, I):
     """A down bias of 2^17 on output features 0..63 puts those y chunks beyond
     fp16's range: they stay f32 while the rest of each row is stored in fp16
-    (an fp16 store of them would be inf).  The two column ranges are compared
-    separately, so the in-range chunks meet the bar on their own scale."""
-    cfg = synth.MoeConfig(name="yovf", cid=210, T=300, H=320, I=256, E=4, K=2,
+    (an fp16 store of them would be inf).  With I = 2304 the down GEMM splits
+    its reduction in two: the bias goes in with split 0 only, so that split's
+    chunk stays f32 while split 1's partial sums of the same chunk are fp16.
+    The two column ranges are compared separately, so the in-range chunks
+    meet the bar on their own scale."""
+    cfg = synth.MoeConfig(name="yovf", cid=210, T=300, H=320, I=I, E=4, K=2,
                           expert_biases=True)
     inp = synth.make_inputs(cfg, device=DEV)
     b = inp["down_bias"].float()
@@ -140,8 +144,8 @@ def test_y_chunks_beyond_fp16_stay_f32(variant):
     assert np.abs(ref[:, :64]).max() > 65504.0
     out, r, _ = run_gpu(cfg, inp, gemm_variant=variant)
     check_routing(cfg, inp, r, cfg.T)
-    compare_out(out[:, :64], ref[:, :64], "bf16", f"y chunk beyond fp16, variant {variant}")
-    compare_out(out[:, 64:], ref[:, 64:], "bf16", f"y chunks in fp16, variant {variant}")
+    compare_out(out[:, :64], ref[:, :64], "bf16", f"y chunk beyond fp16, I={I} variant {variant}")
+    compare_out(out[:, 64:], ref[:, 64:], "bf16", f"y chunks in fp16, I={I} variant {variant}")
 
 
 # ------------------------------------------------------------------ edge cases
