@@ -17,7 +17,11 @@
 // the weights are stored as f32.
 //
 // Lane layout: lane l holds experts l, l+64, l+128, ... (coalesced logit
-// loads); argmax steps are butterfly shuffles across the wavefront.
+// loads).  Argmax and max run as all-reductions over the wavefront: within
+// each 16-lane row by DPP lane moves (quad swaps, then the half-row and row
+// mirrors: each step pairs lanes that hold disjoint groups), across rows by
+// two shuffles.  The result is the best element of a total order, so the
+// pairing order cannot change it.
 // Every argmax runs over a set that still holds a candidate (validated
 // options guarantee >= K eligible experts), and a NaN key counts as -inf, so
 // every stored id is a real expert index.
@@ -40,10 +44,45 @@ __device__ inline bool better(double k1, int i1, double k2, int i2)
     return k1 > k2 || (k1 == k2 && i1 < i2);
 }
 
+// value of lane (lane's partner under DPP control CTRL) within its 16-lane row
+template <int CTRL>
+__device__ inline int dpp(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+
+template <int CTRL>
+__device__ inline double dpp(double v)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// DPP controls: quad permutations [1,0,3,2] and [2,3,0,1], half-row mirror
+// (lane i <-> 7 - i within 8), row mirror (i <-> 15 - i within 16)
+constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e, kHalfMirror = 0x141, kMirror = 0x140;
+
+template <int CTRL>
+__device__ inline void argmax_step_dpp(KeyIdx &v)
+{
+    const double ok = dpp<CTRL>(v.key);
+    const int oi = dpp<CTRL>(v.idx);
+    if (better(ok, oi, v.key, v.idx)) {
+        v.key = ok;
+        v.idx = oi;
+    }
+}
+
 __device__ inline KeyIdx wave_argmax(KeyIdx v)
 {
+    argmax_step_dpp<kQuadXor1>(v);
+    argmax_step_dpp<kQuadXor2>(v);
+    argmax_step_dpp<kHalfMirror>(v);
+    argmax_step_dpp<kMirror>(v);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
+    for (int off = 16; off <= 32; off <<= 1) {
         double ok = __shfl_xor(v.key, off, 64);
         int oi = __shfl_xor(v.idx, off, 64);
         if (better(ok, oi, v.key, v.idx)) {
@@ -56,10 +95,21 @@ __device__ inline KeyIdx wave_argmax(KeyIdx v)
 
 __device__ inline double wave_max(double v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v = fmax(v, __shfl_xor(v, off, 64));
-    return v;
+    v = fmax(v, dpp<kQuadXor1>(v));
+    v = fmax(v, dpp<kQuadXor2>(v));
+    v = fmax(v, dpp<kHalfMirror>(v));
+    v = fmax(v, dpp<kMirror>(v));
+    v = fmax(v, __shfl_xor(v, 16, 64));
+    return fmax(v, __shfl_xor(v, 32, 64));
+}
+
+// lane `src` (the same for every lane)'s value, through a scalar register
+__device__ inline double lane_value(double v, int src)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 __device__ inline double wave_sum(double v)
@@ -179,7 +229,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
             if (i == slot) sc = score[i];
-        sc = __shfl(sc, owner, 64);
+        sc = lane_value(sc, __builtin_amdgcn_readfirstlane(owner));
         if (lane == owner) {
 #pragma unroll
             for (int i = 0; i < EPL; ++i)
@@ -194,7 +244,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
     // weights: renormalise (sum in slot order, clamped at 2^-14), then scale
     if (a.renormalize) {
         double s = 0.0;
-        for (int j = 0; j < a.K; ++j) s += __shfl(my_w, j, 64);
+        for (int j = 0; j < a.K; ++j) s += lane_value(my_w, j);
         const double d = s > 0x1p-14 ? s : 0x1p-14;
         my_w = my_w / d;
     }
