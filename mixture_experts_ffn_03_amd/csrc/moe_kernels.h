@@ -30,7 +30,7 @@ struct PermuteArgs {
     const int32_t *ids;      // [T, K]
     int T, E, K;
     int32_t *block_counts;   // [NB, E]   NB = ceil(T / kPermTokens)
-    int32_t *block_base;     // [NB, E]
+    int32_t *block_base;     // [NB, E] rows of expert e in blocks before b
     int32_t *counts;         // [E]
     int32_t *offsets;        // [E + 1]
     int32_t *row_token;      // [T*K]

@@ -123,18 +123,25 @@ __global__ __launch_bounds__(1024) void scan_kernel(PermuteArgs a)
     __shared__ int buf[16 * 5];
     const int e = threadIdx.x;
     const int NB = (a.T + kPermTokens - 1) / kPermTokens;
+    // block_base gets expert e's rows before each block, within the expert
+    // (the scatter adds the expert's offset); the counts are read 16 blocks
+    // at a time, so their loads overlap instead of one round trip per block
     int run = 0;
     if (e < a.E) {
-        for (int b = 0; b < NB; ++b) {
-            const int64_t i = (int64_t)b * a.E + e;
-            const int c = a.block_counts[i];
-            a.block_base[i] = run;
-            run += c;
+        for (int b0 = 0; b0 < NB; b0 += 16) {
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                c[i] = b0 + i < NB ? a.block_counts[(int64_t)(b0 + i) * a.E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (b0 + i < NB) {
+                    a.block_base[(int64_t)(b0 + i) * a.E + e] = run;
+                    run += c[i];
+                }
         }
     }
-    const int off = scan_experts(a, run, buf);
-    if (e < a.E)
-        for (int b = 0; b < NB; ++b) a.block_base[(int64_t)b * a.E + e] += off;
+    scan_experts(a, run, buf);
 }
 
 // Rows of the pairs of tokens [t0, t0 + kPermTokens) from the block's masks;
@@ -164,7 +171,9 @@ __global__ __launch_bounds__(kPermTokens) void scatter_kernel(PermuteArgs a)
     extern __shared__ uint32_t masks[];
     const int t0 = blockIdx.x * kPermTokens;
     build_masks(a, masks, t0);
-    scatter_block(a, masks, t0, [&](int e) { return a.block_base[(int64_t)blockIdx.x * a.E + e]; });
+    scatter_block(a, masks, t0, [&](int e) {
+        return a.offsets[e] + a.block_base[(int64_t)blockIdx.x * a.E + e];
+    });
 }
 
 // T <= kPermTokens (decode sizes): one token block, so masks, scan and
