@@ -103,6 +103,37 @@ __device__ inline double wave_max(double v)
     return fmax(v, __shfl_xor(v, 32, 64));
 }
 
+// The two best (key, idx) of a lane's set, best first; missing entries are
+// (-inf, kNone).
+struct Top2 {
+    double k1, k2;
+    int i1, i2;
+};
+
+// union of two disjoint sets' best two
+__device__ inline Top2 merge_top2(Top2 a, Top2 b)
+{
+    // first: the better of the two firsts; second: the better of the other
+    // list's first and the winning list's second
+    const bool bw = better(b.k1, b.i1, a.k1, a.i1);
+    const double f_k = bw ? b.k1 : a.k1, o_k = bw ? a.k1 : b.k1, s_k = bw ? b.k2 : a.k2;
+    const int f_i = bw ? b.i1 : a.i1, o_i = bw ? a.i1 : b.i1, s_i = bw ? b.i2 : a.i2;
+    const bool ow = better(o_k, o_i, s_k, s_i);
+    return Top2{f_k, ow ? o_k : s_k, f_i, ow ? o_i : s_i};
+}
+
+template <int CTRL>
+__device__ inline Top2 top2_step_dpp(Top2 v)
+{
+    return merge_top2(v, Top2{dpp<CTRL>(v.k1), dpp<CTRL>(v.k2), dpp<CTRL>(v.i1), dpp<CTRL>(v.i2)});
+}
+
+__device__ inline Top2 top2_step_shfl(Top2 v, int off)
+{
+    return merge_top2(v, Top2{__shfl_xor(v.k1, off, 64), __shfl_xor(v.k2, off, 64),
+                              __shfl_xor(v.i1, off, 64), __shfl_xor(v.i2, off, 64)});
+}
+
 // lane `src` (the same for every lane)'s value, through a scalar register
 __device__ inline double lane_value(double v, int src)
 {
@@ -174,6 +205,36 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
     if (a.n_group > 0) {
         const int gs = E / a.n_group;
         double my_gscore = -INFINITY;   // lane g holds the score of group g
+        if ((gs & (gs - 1)) == 0 && gs <= 64) {
+            // groups of 2^n <= 64 experts are aligned lane segments of one
+            // slot: a top-2 all-reduction within segments (DPP moves up to 16
+            // lanes, then shuffles) gives every group's two best keys at once
+            double gsum_slot[EPL];
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane + 64 * i;
+                Top2 v{live[i] ? key[i] : -INFINITY, -INFINITY, live[i] ? e : kNone, kNone};
+                if (gs >= 2) v = top2_step_dpp<kQuadXor1>(v);
+                if (gs >= 4) v = top2_step_dpp<kQuadXor2>(v);
+                if (gs >= 8) v = top2_step_dpp<kHalfMirror>(v);
+                if (gs >= 16) v = top2_step_dpp<kMirror>(v);
+                if (gs >= 32) v = top2_step_shfl(v, 16);
+                if (gs >= 64) v = top2_step_shfl(v, 32);
+                double gsum = v.k1;
+                if (gs >= 2) {
+                    gsum = v.k1 + v.k2;
+                    if (gsum != gsum) gsum = -INFINITY;
+                }
+                gsum_slot[i] = gsum;
+            }
+            // group g's first expert g * gs sits in slot g * gs / 64
+            const int src = (lane * gs) & 63, src_slot = (lane * gs) >> 6;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const double v = __shfl(gsum_slot[i], src, 64);
+                if (lane < a.n_group && src_slot == i) my_gscore = v;
+            }
+        } else
         for (int g = 0; g < a.n_group; ++g) {
             KeyIdx b1{-INFINITY, kNone};
 #pragma unroll

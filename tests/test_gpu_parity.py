@@ -220,6 +220,35 @@ def test_expert_counts(E, K):
     compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"E={E} K={K}")
 
 
+@pytest.mark.parametrize("E,G,TG,K", [(64, 64, 8, 4), (64, 32, 4, 4), (128, 2, 1, 8),
+                                       (96, 3, 2, 4), (48, 3, 2, 4), (60, 5, 2, 4),
+                                       (256, 2, 1, 8)])
+def test_group_shapes(E, G, TG, K):
+    """Group-limited routing at group sizes 1, 2, 64, 32 and 16 with padding
+    lanes past E (one top-2 reduction over lane segments), and 12 and 128
+    (group by group): ids and counts bit-exact."""
+    cfg = synth.MoeConfig(name="grp", cid=211, T=257, H=64, I=64, E=E, K=K,
+                          scoring="sigmoid", selection_bias_std=0.1, n_group=G,
+                          topk_group=TG, renormalize=True)
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, _ = run_gpu(cfg, inp)
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"groups E={E} G={G} TG={TG}")
+
+
+def test_group_ties():
+    """Equal logits and no selection bias with 8 groups of 8: every group sum
+    ties, so the lowest groups and the lowest experts in them win."""
+    cfg = synth.MoeConfig(name="gtie", cid=212, T=40, H=64, I=64, E=64, K=4,
+                          n_group=8, topk_group=2)
+    inp = synth.make_inputs(cfg, device=DEV)
+    inp["logits"] = torch.zeros_like(inp["logits"])
+    out, r, _ = run_gpu(cfg, inp)
+    ids = r["topk_ids"].cpu().numpy()
+    assert (ids == np.arange(4)[None, :]).all(), ids[:3]
+    check_routing(cfg, inp, r, cfg.T)
+
+
 def test_ties_and_equal_logits():
     """Equal logits everywhere: ids 0..K-1 on every token (lower index wins)."""
     cfg = synth.MoeConfig(name="tie", cid=206, T=40, H=64, I=64, E=16, K=4)
