@@ -7,7 +7,7 @@
 // token panel the "B" operand, so each lane ends with four consecutive output
 // features of one token -- 8-byte 16-bit / 16-byte f32 stores in the epilogue.
 //
-// Two epilogues:
+// Epilogues (EpiMode):
 //  gated  (gate||up GEMM, ONNX "MoE" fc1/fc3): the BN weight rows of a tile
 //         are BN/2 gate rows and the BN/2 up rows of the same features; a
 //         wave holds the gate and up accumulators of the same features in
@@ -15,15 +15,19 @@
 //         h is stored in fp16 (11-bit significand, 8x finer than bf16) when
 //         the whole tile fits fp16's range and the down weights convert
 //         exactly, else in bf16; one format byte per tile records the choice.
+//  act    (fc1 of a non-gated expert): the activation of every feature,
+//         stored like the gated h.
 //  down   (ONNX "MoE" fc2): when every h tile of its rows is fp16 (the
-//         normal case), a workgroup converts the bf16 (or MXFP4) down weights
-//         exactly to fp16 after their LDS read and runs the f16 MFMA;
-//         otherwise it rounds the fp16 h fragments to bf16 and runs the bf16
-//         MFMA.  Adds the down bias and stores y (or, with a split reduction,
-//         each split's partial sums) per 64-feature chunk of a row: fp16 when
-//         the chunk fits fp16's range (half the bytes the combine reads back),
-//         else f32, with one format byte per chunk.  The combine rounds to the
-//         output dtype once, after the weighted sum.
+//         normal case), a workgroup runs the f16 MFMA on the prepared fp16
+//         copy of the down weights, or, without one, converts the bf16 (or
+//         MXFP4) weights exactly to fp16 after their LDS read; otherwise it
+//         rounds the fp16 h fragments to bf16 and runs the bf16 MFMA.  Adds
+//         the down bias and stores y (or, with a split reduction, each
+//         split's partial sums) per 64-feature chunk of a row: fp16 when the
+//         chunk fits fp16's range (half the bytes the combine reads back),
+//         else f32, with one format byte per chunk.  The combine rounds to
+//         the output dtype once, after the weighted sum.
+//  plain  (the router GEMM): x times the transposed router weights, f32 out.
 //
 // The token operand of the gated GEMM is gathered straight from x through the
 // permutation (row_token), so the permuted activations are never written.
