@@ -621,6 +621,14 @@ using PrefillDTile = DTile<256, 256, 64, 4, 2, 2, 3, false>;
 // reads less LDS per MFMA but leaves the SIMDs of the lower half idle or
 // short on a partial tile).
 using PrefillFcTile = DTile<256, 256, 64, 4, 1, 2, 3, false, 1>;
+// Its loop body for a tile of at most 128 rows (the 256-row schedule gives
+// one to each expert with that few): token stages of half the size leave room
+// for a fourth weight stage in the same 160 KiB, and such a tile, with half
+// the MFMA work per k-step, waits on its weight stream.
+using ShortFcTile = DTile<256, 128, 64, 4, 1, 2, 4, false, 1>;
+static_assert(ShortFcTile::NT == PrefillFcTile::NT && ShortFcTile::WPE == PrefillFcTile::WPE &&
+                  ShortFcTile::LDS_BYTES <= PrefillFcTile::LDS_BYTES,
+              "the short body runs in the 256-row tile's workgroup and LDS");
 // 256 threads, wave 64x32; weights stream from HBM: four B stages.
 using DecodeDTile = DTile<256, 32, 64, 4, 1, 2, 4, false>;
 // The down GEMM at decode sizes has short reductions (I / 64 k-steps): two
@@ -1132,6 +1140,12 @@ __global__ __launch_bounds__(TL::NT, TL::WPE) void gemm_dma_kernel(GemmArgs g)
         const bool f16 = *flag != 0;
         __syncthreads();                     // before the loads overwrite it
         if (f16 && !TL::MX && g.w_f16) {
+            if constexpr (std::is_same<TL, PrefillFcTile>::value) {
+                if (tw.nrows <= ShortFcTile::BM && !ragged) {
+                    dma_body<ShortFcTile, EPI, true, false, true>(g, tw, lds, s_red);
+                    return;
+                }
+            }
             if (ragged) dma_body<TL, EPI, true, true, !TL::MX>(g, tw, lds, s_red);
             else dma_body<TL, EPI, true, false, !TL::MX>(g, tw, lds, s_red);
         } else if (TL::WPE != 1 && f16) {
@@ -1146,6 +1160,12 @@ __global__ __launch_bounds__(TL::NT, TL::WPE) void gemm_dma_kernel(GemmArgs g)
         }
     } else {
         __syncthreads();                     // every s_cum read is done
+        if constexpr (std::is_same<TL, PrefillFcTile>::value && EPI == kEpiGated) {
+            if (tw.nrows <= ShortFcTile::BM && !ragged) {
+                dma_body<ShortFcTile, EPI, false, false>(g, tw, lds, s_red);
+                return;
+            }
+        }
         if (ragged) dma_body<TL, EPI, false, true>(g, tw, lds, s_red);
         else dma_body<TL, EPI, false, false>(g, tw, lds, s_red);
     }
