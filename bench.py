@@ -3,14 +3,27 @@
 
 One step = one full forward of the layer (routing, permutation, grouped
 gate||up GEMM with the fused activation, grouped down GEMM, combine) over one
-batch of synthetic, seeded inputs already resident in HBM.  The default
+batch of synthetic, seeded inputs already resident in HBM.  The headline
 workload is the Mixtral-8x7B-shaped prefill layer (T=4096, H=4096, I=14336,
-E=8, top-2, bf16, split gate||up, softmax renormalised, SiLU-gated).
+E=8, top-2, bf16, split gate||up, softmax renormalised, SiLU-gated): its K
+back-to-back steps are the timed region, bracketed by device synchronisation.
 
-Prints ONE JSON line (the last line of stdout).  The dominant kernel's
-duration is measured live with HIP events recorded by the library around
-each stage on the launch stream (moe_forward_timed).  The CPU baseline is the
-fp64 oracle timed on a bounded token sample of the same workload.
+Prints ONE JSON line (the last line of stdout).  Besides the headline figures
+it carries:
+  - "decode": the Qwen3-30B-A3B-shaped decode step (T=32), whose metric is
+    the weight-stream rate (touched experts' weight bytes per step);
+  - "workloads": the gpt-oss-20b-shaped MXFP4 layer and the DeepSeek-V3-shaped
+    layer (and the decode step again), each with its own roofline object.
+Each of these is timed step by step with HIP events on the launch stream,
+with a >= 512 MiB scratch write between steps (outside the events) so that a
+step never finds the previous step's weights in the 256 MiB Infinity Cache.
+The headline's timed loop has no such write: its 2.8 GB of weights cycle the
+cache by themselves; its per-step flushed time is reported next to it.
+
+The dominant kernel's duration is measured live with HIP events recorded by
+the library around each stage on the launch stream (moe_forward_timed).  The
+CPU baseline is the fp64 oracle timed on a bounded token sample of the
+headline workload.
 """
 import argparse
 import ctypes as C
@@ -28,6 +41,7 @@ METRIC = ("MoE layer active TFLOP/s + tokens/s (prefill); weight-stream HBM GB/s
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 STAGES = ["route", "permute", "gemm_gate_up", "gemm_down", "combine"]
+FLUSH_BYTES = 1 << 30       # scratch written between flushed steps (4x the MALL)
 
 
 def log(*a):
@@ -35,7 +49,8 @@ def log(*a):
 
 
 class Hip:
-    """Raw HIP events through libamdhip64 (recorded by the library itself)."""
+    """Raw HIP events through libamdhip64 (recorded by the library itself, or
+    on torch's current stream, which is the stream the layer launches on)."""
 
     def __init__(self):
         self.L = C.CDLL("libamdhip64.so")
@@ -86,6 +101,29 @@ def load_traffic(workload: str):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    """Threads the CPU baseline may use: the CPUs this process may run on,
+    capped by OMP_NUM_THREADS when the host sets it (a shared GPU host gives
+    each GPU's jobs a fixed CPU share and says so there)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    n = min(avail, int(cap)) if cap and cap.isdigit() and int(cap) > 0 else avail
+    return n, avail
+
+
 def cpu_baseline(cfg, inp, budget_s: float, stream_bytes=None):
     """The oracle on the host cores over a bounded token sample.  With
     stream_bytes (a decode step) and the whole step in the sample, the rate is
@@ -93,7 +131,7 @@ def cpu_baseline(cfg, inp, budget_s: float, stream_bytes=None):
     import numpy as np
     import oracle
     oracle.build()
-    threads = min(os.cpu_count() or 1, 16)
+    threads, avail = host_threads()
     host = {k: v.cpu() for k, v in inp.items()}
     p = oracle.params_of(cfg)
     rng = np.random.default_rng(1)
@@ -111,9 +149,114 @@ def cpu_baseline(cfg, inp, budget_s: float, stream_bytes=None):
         value, unit = stream_bytes / dt / 1e9, "GB/s"
     else:
         value, unit = cfg.flops / cfg.T * len(toks) / dt / 1e12, "TFLOP/s"
+    cap = os.environ.get("OMP_NUM_THREADS")
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "cpus_available": avail,
+            "cores_note": (f"capped at OMP_NUM_THREADS={cap}, the host's CPU share per GPU"
+                           if cap and threads < avail else "all CPUs available to the process"),
             "sample": f"{len(toks)} of {cfg.T} tokens of {cfg.name} (full weights), "
                       f"{dt:.3g} s on {threads} threads; {len(toks) / dt:.2f} tokens/s"}
+
+
+class Workload:
+    """One workload's inputs, layer and per-step accounting."""
+
+    def __init__(self, cfg, dev, gemm_variant=0):
+        from mixture_experts_ffn_03_amd import from_config, synth
+        import torch
+        self.cfg = cfg
+        log(f"[bench] generating {cfg.name} inputs on {dev}")
+        self.inp = synth.make_inputs(cfg, device=dev)
+        self.layer = from_config(cfg, gemm_variant=gemm_variant)
+        self.layer.set_weights_from(self.inp)
+        self.layer.initialize()
+        self.x, lg = self.inp["x"], self.inp["logits"]
+        self.out = torch.empty_like(self.x)
+        self.ws = self.layer.workspace(cfg.T, dev)
+        # with the layer's own router the step computes the logits itself
+        self.step_logits = None if cfg.router else lg
+        if cfg.router:
+            lg = self.layer.router_logits(self.x)
+        # experts that receive tokens (their weights are the ones a step streams)
+        self.touched = int((self.layer.route(lg)["expert_counts"] > 0).sum().item())
+        wb = 0.5 + 1.0 / 32.0 if cfg.w_dtype == "mxfp4" else (4.0 if cfg.w_dtype == "f32" else 2.0)
+        self.gu_bytes = (2.0 if cfg.gated else 1.0) * cfg.I * cfg.H * wb
+        self.dn_bytes = 1.0 * cfg.H * cfg.I * wb
+        # few rows per expert: the step streams weights (the threshold the
+        # library uses to pick its small-M tiles)
+        self.decode = cfg.T * cfg.K < 96 * cfg.E
+        torch.cuda.synchronize()
+
+    def step(self, events=None):
+        self.layer(self.x, self.step_logits, out=self.out, workspace=self.ws, events=events)
+
+    def stream_bytes(self) -> float:
+        return self.touched * (self.gu_bytes + self.dn_bytes)
+
+    def summary(self, ms: float, stage_ms: dict, flushed: bool) -> dict:
+        """Rates of one workload from its step time and stage times, with the
+        roofline object of its gate||up GEMM (the dominant kernel)."""
+        cfg = self.cfg
+        g1 = stage_ms["gemm_gate_up"]
+        gemm1_flops = (4.0 if cfg.gated else 2.0) * cfg.T * cfg.K * cfg.H * cfg.I
+        d = {
+            "workload": cfg.name, "ms_per_step": ms,
+            "active_tflops": cfg.flops / (ms * 1e-3) / 1e12,
+            "tokens_per_s": cfg.T / (ms * 1e-3),
+            "weight_stream_gbs": self.stream_bytes() / (ms * 1e-3) / 1e9,
+            "experts_touched": self.touched,
+            "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+            "mall_flushed_between_steps": flushed,
+            "gemm_ms": round(g1 + stage_ms["gemm_down"], 4),
+        }
+        if self.decode:
+            g1_bytes = (self.touched * self.gu_bytes + cfg.T * cfg.H * 2
+                        + cfg.T * cfg.K * cfg.I * 2)
+            roof = {"bound": "hbm", "kernel": "gate||up grouped GEMM (decode tiles)",
+                    "achieved": g1_bytes / (g1 * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s"}
+            d["gemms_weight_stream_gbs"] = self.stream_bytes() / (d["gemm_ms"] * 1e-3) / 1e9
+            d["gemms_hbm_frac"] = d["gemms_weight_stream_gbs"] / PEAK_HBM_GBS
+        else:
+            roof = {"bound": "mfma", "kernel": "gate||up grouped GEMM",
+                    "achieved": gemm1_flops / (g1 * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s"}
+            gemm2_flops = 2.0 * cfg.T * cfg.K * cfg.H * cfg.I
+            d["gemm_down_frac"] = gemm2_flops / (stage_ms["gemm_down"] * 1e-3) / 1e12 \
+                / PEAK_BF16_TFLOPS
+            d["gemms_frac"] = cfg.flops / (d["gemm_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = load_traffic(cfg.name)
+        d["roofline"] = roof
+        return d
+
+
+def stage_times(hip, evs):
+    out = {}
+    for i, name in enumerate(STAGES):
+        out[name] = sum(hip.elapsed_ms(row[i], row[i + 1]) for row in evs) / len(evs)
+    return out
+
+
+def timed_flushed(wl, hip, steps: int, warmup: int, scratch):
+    """Step by step with a scratch write of FLUSH_BYTES before each step,
+    outside the step's events.  Returns (mean ms, stage ms, min ms)."""
+    import torch
+    for _ in range(warmup):
+        scratch.fill_(1)
+        wl.step()
+    torch.cuda.synchronize()
+    evs = [[hip.event() for _ in range(6)] for _ in range(steps)]
+    for k in range(steps):
+        scratch.fill_(k & 0xff)
+        wl.step(events=evs[k])
+    torch.cuda.synchronize()
+    per = [hip.elapsed_ms(row[0], row[5]) for row in evs]
+    st = stage_times(hip, evs)
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+    return sum(per) / len(per), st, min(per)
 
 
 def main():
@@ -124,6 +267,10 @@ def main():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="headline workload only (no decode / gpt-oss / DeepSeek sub-results)")
+    ap.add_argument("--sub-steps", type=int, default=10,
+                    help="flushed steps timed per sub-result workload")
     ap.add_argument("--activation", default=None,
                     help="override the workload's activation (e.g. relu, gelu, identity)")
     ap.add_argument("--weigh-inputs", action="store_true",
@@ -142,7 +289,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from mixture_experts_ffn_03_amd import from_config, synth
+    from mixture_experts_ffn_03_amd import synth
 
     cfg = synth.CONFIGS[args.workload]
     over = {}
@@ -155,26 +302,7 @@ def main():
     if over:
         cfg = cfg.replace(**over)
     dev = torch.device("cuda:0")
-    log(f"[bench] generating {cfg.name} inputs on {dev}")
-    inp = synth.make_inputs(cfg, device=dev)
-    layer = from_config(cfg, gemm_variant=args.gemm_variant)
-    layer.set_weights_from(inp)
-    x, lg = inp["x"], inp["logits"]
-    out = torch.empty_like(x)
-    ws = layer.workspace(cfg.T, dev)
-    # with the layer's own router the step computes the logits itself
-    step_logits = None if cfg.router else lg
-    if cfg.router:
-        lg = layer.router_logits(x)
-    # experts that receive tokens (their weights are the ones a step streams)
-    touched = int((layer.route(lg)["expert_counts"] > 0).sum().item())
-    wb = 0.5 + 1.0 / 32.0 if cfg.w_dtype == "mxfp4" else (4.0 if cfg.w_dtype == "f32" else 2.0)
-    gu_bytes = (2.0 if cfg.gated else 1.0) * cfg.I * cfg.H * wb
-    dn_bytes = 1.0 * cfg.H * cfg.I * wb
-    # few rows per expert: the step streams weights (same threshold the library
-    # uses to pick its small-M tiles)
-    decode = cfg.T * cfg.K < 96 * cfg.E
-    torch.cuda.synchronize()
+    wl = Workload(cfg, dev, args.gemm_variant)
 
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -182,55 +310,43 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         log("[bench] copy calibration: 268435456 bytes read + written")
+        del a, b
 
     hip = Hip()
     evs = [[hip.event() for _ in range(6)] for _ in range(args.steps)]
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
-        layer(x, step_logits, out=out, workspace=ws)
+        wl.step()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
     start.record()
     for k in range(args.steps):
-        layer(x, step_logits, out=out, workspace=ws, events=evs[k])
+        wl.step(events=evs[k])
     end.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms = total_ms / args.steps
-    stage_ms = {}
-    for i, name in enumerate(STAGES):
-        stage_ms[name] = sum(hip.elapsed_ms(evs[k][i], evs[k][i + 1])
-                             for k in range(args.steps)) / args.steps
+    ms = start.elapsed_time(end) / args.steps
+    stage_ms = stage_times(hip, evs)
     for row in evs:
         for e in row:
             hip.destroy(e)
+    head = wl.summary(ms, stage_ms, flushed=False)
 
-    flops = float(cfg.flops)
-    gemm1_flops = (4.0 if cfg.gated else 2.0) * cfg.T * cfg.K * cfg.H * cfg.I
-    g1 = stage_ms["gemm_gate_up"]
-    traffic = load_traffic(cfg.name)
-    if decode:
-        # weight-stream rate: each touched expert's weights are read once per step
-        stream = touched * (gu_bytes + dn_bytes)
-        value, unit = stream / (ms * 1e-3) / 1e9, "GB/s"
-        g1_bytes = touched * gu_bytes + cfg.T * cfg.H * 2 + cfg.T * cfg.K * cfg.I * 2
-        roof = {"bound": "hbm", "kernel": "gate||up grouped GEMM (decode tiles)",
-                "achieved": g1_bytes / (g1 * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s"}
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    fl_ms, fl_st, fl_min = timed_flushed(wl, hip, min(args.steps, 10), 1, scratch)
+    log(f"[bench] {cfg.name}: {ms:.4f} ms/step back to back, {fl_ms:.4f} flushed")
+
+    if wl.decode:
+        value, unit = wl.stream_bytes() / (ms * 1e-3) / 1e9, "GB/s"
     else:
-        value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
-        roof = {"bound": "mfma", "kernel": "gate||up grouped GEMM",
-                "achieved": gemm1_flops / (g1 * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic
+        value, unit = cfg.flops / (ms * 1e-3) / 1e12, "TFLOP/s"
     res = {
         "metric": METRIC,
         "value": value,
         "unit": unit,
-        "tokens_per_s": cfg.T / (ms * 1e-3),
+        "tokens_per_s": head["tokens_per_s"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -245,17 +361,51 @@ def main():
                    "scoring": cfg.scoring, "activation": cfg.activation,
                    "weigh_inputs": cfg.weigh_inputs, "router_in_step": cfg.router,
                    "parallelism": "none (1 GPU)"},
-        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "active_tflops": flops / (ms * 1e-3) / 1e12,
-        "weight_stream_gbs": touched * (gu_bytes + dn_bytes) / (ms * 1e-3) / 1e9,
-        "experts_touched": touched,
-        "roofline": roof,
+        "stages_ms": head["stages_ms"],
+        "active_tflops": head["active_tflops"],
+        "weight_stream_gbs": head["weight_stream_gbs"],
+        "experts_touched": wl.touched,
+        "gemms_frac": head.get("gemms_frac"),
+        "flushed": {"ms_per_step": fl_ms, "min_ms": fl_min,
+                    "stages_ms": {k: round(v, 4) for k, v in fl_st.items()},
+                    "scratch_bytes": FLUSH_BYTES},
+        "roofline": head["roofline"],
     }
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(
-            cfg, inp, args.cpu_seconds,
-            stream_bytes=touched * (gu_bytes + dn_bytes) if decode else None)
+        res["cpu_baseline"] = cpu_baseline(cfg, wl.inp, args.cpu_seconds,
+                                           stream_bytes=wl.stream_bytes() if wl.decode else None)
+
+    if not args.no_sub and not over and args.gemm_variant == 0:
+        subs = {}
+        headline = cfg.name
+        del wl
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        for name in ("qwen3_decode", "gptoss_mxfp4", "deepseek_v3"):
+            if name == headline:
+                continue
+            sw = Workload(synth.CONFIGS[name], dev)
+            s_ms, s_st, s_min = timed_flushed(sw, hip, args.sub_steps, 2, scratch)
+            d = sw.summary(s_ms, s_st, flushed=True)
+            d["min_ms"] = s_min
+            log(f"[bench] {name}: {s_ms:.4f} ms/step (flushed), gate||up "
+                f"{d['roofline']['frac']:.3f} of {d['roofline']['bound']} peak")
+            subs[name] = d
+            del sw
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        res["workloads"] = subs
+        if "qwen3_decode" in subs:
+            q = subs["qwen3_decode"]
+            res["decode"] = {
+                "workload": "qwen3_decode", "metric": "weight-stream HBM GB/s (decode)",
+                "value": q["weight_stream_gbs"], "unit": "GB/s",
+                "hbm_frac_step": q["weight_stream_gbs"] / PEAK_HBM_GBS,
+                "gemms_weight_stream_gbs": q["gemms_weight_stream_gbs"],
+                "gemms_hbm_frac": q["gemms_hbm_frac"],
+                "ms_per_step": q["ms_per_step"], "mall_flushed_between_steps": True,
+                "roofline": q["roofline"]}
     print(json.dumps(res), flush=True)
 
 

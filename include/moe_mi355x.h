@@ -127,7 +127,10 @@ typedef struct moe_options {
                                      of device memory, made by moe_prepare, freed by
                                      moe_destroy), so the fp16 down GEMM streams it
                                      instead of converting each tile's weights in
-                                     registers.  If the allocation fails the layer
+                                     registers, and the forward no longer reads the
+                                     caller's down stack, which the caller may then
+                                     release (moe_borrowed_slots): one resident
+                                     copy.  If the allocation fails the layer
                                      converts per tile instead, without error.
                                      0 or 1; default 1                              */
 } moe_options;
@@ -218,11 +221,44 @@ moe_status moe_create(int64_t num_experts, int64_t hidden_size,
 moe_status moe_set_weights(moe_layer *layer, const moe_weights *w);
 
 /* Optional warm-up (QMoEWoQ::initialize, "pack once"): checks that every
- * declared slot is bound, scans the down weights for exact fp16 conversion,
- * packs MXFP4 stacks into the layout the GEMMs stream and transposes a bound
- * router.  Runs once per binding (a forward runs it if needed) and
- * synchronises `stream`.  Errors: UNBOUND, HIP. */
+ * declared slot is bound, scans the down weights for fp16's range (a 16-bit
+ * down stack whose magnitudes stay within it converts exactly in fp16's
+ * normal range; a value below 2^-14 keeps the fewer bits of an fp16
+ * subnormal, an absolute error of at most 2^-25), packs MXFP4 stacks into
+ * the layout the GEMMs stream, makes the fp16 down copy (down_fp16_copy)
+ * and transposes a bound router.  Runs once per binding (a forward runs it
+ * if needed) and synchronises `stream`.  Errors: UNBOUND, HIP. */
 moe_status moe_prepare(moe_layer *layer, void *stream);
+
+/* Bits of moe_borrowed_slots, one per moe_weights member in field order. */
+#define MOE_SLOT_GATE_UP_EXPERTS 0x001u
+#define MOE_SLOT_DOWN_EXPERTS 0x002u
+#define MOE_SLOT_GATE_EXPERTS 0x004u
+#define MOE_SLOT_GATE_UP_BIAS 0x008u
+#define MOE_SLOT_DOWN_BIAS 0x010u
+#define MOE_SLOT_GATE_BIAS 0x020u
+#define MOE_SLOT_E_SCORE_CORRECTION_BIAS 0x040u
+#define MOE_SLOT_ROUTER_WEIGHT 0x080u
+#define MOE_SLOT_ROUTER_BIAS 0x100u
+
+/* Which bound caller buffers a forward still reads (the clika
+ * "ClikaRT::nn::QMoEWoQ" class description: once packed, the layer keeps one
+ * resident copy of its weights).  Sets *mask to the MOE_SLOT_* bits of the
+ * bound slots whose caller buffer moe_forward, moe_route and
+ * moe_router_logits read.  Before the binding is prepared every bound slot is
+ * borrowed.  After moe_prepare:
+ *  - MXFP4 layers read only the library's packed copy of gate_up_experts,
+ *    gate_experts and down_experts (codes and scales);
+ *  - 16-bit layers whose prepare made the fp16 down copy (down weights in
+ *    fp16's range, down_fp16_copy = 1, the allocation succeeded) read that
+ *    copy instead of down_experts, including the bf16 fallback for h tiles
+ *    beyond fp16's range;
+ *  - a bound router is read from its transposed copy, not router_weight.
+ * A slot whose bit is clear may be released or overwritten by the caller
+ * until the next moe_set_weights (which drops the prepared state and makes
+ * every slot borrowed again).  Biases and the gate||up stack of 16-bit layers
+ * stay borrowed.  Errors: INVALID_ARGUMENT, UNBOUND. */
+moe_status moe_borrowed_slots(const moe_layer *layer, uint32_t *mask);
 
 /* Device workspace bytes a forward (or moe_route) on T tokens needs.  The
  * caller allocates it (256-byte aligned) and may reuse it across calls that

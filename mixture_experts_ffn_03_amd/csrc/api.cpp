@@ -4,6 +4,7 @@
 // (make, set_weights, initialize, forward, to) and the Python "MoE" page
 // (constructor, set_weights slot names, forward signature).
 #include "../../include/moe_mi355x.h"
+#include "api_internal.h"
 #include "moe_kernels.h"
 
 #include <hip/hip_runtime.h>
@@ -25,7 +26,7 @@ struct moe_layer {
     moe_weights w;
     bool bound;
     // Prepared state (QMoEWoQ "pack once, thread-safe"): whether the down
-    // weights convert exactly to fp16, which enables the fp16 down GEMM, and
+    // weights lie in fp16's range, which enables the fp16 down GEMM, and
     // for MXFP4 weights the library-owned packed copy the GEMMs stream
     // (allocated at the first prepare, sized by the geometry alone, refilled
     // by every later prepare, freed by moe_destroy).
@@ -426,7 +427,9 @@ moe_status check_workspace(const moe_layer *l, int64_t T, void *ws, size_t bytes
 
 // Prepare once per binding: scan the down-weight range on `s` and decide
 // whether the down GEMM may run in fp16 (bf16 magnitudes <= 65280, or MXFP4
-// scale bytes in [104, 140], convert exactly).  Synchronises `s` once.
+// scale bytes in [104, 140]: every value then converts to fp16 exactly in
+// its normal range, and one below 2^-14 keeps the fewer bits of an fp16
+// subnormal, an absolute error of at most 2^-25).  Synchronises `s` once.
 // Pack an MXFP4 layer's gate||up (GEMM 1, two operands) and down (GEMM 2)
 // stacks into l->mx_pack.
 moe_status pack_mxfp4(const moe_layer *l, hipStream_t s)
@@ -763,9 +766,30 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
                              size_t ws_bytes, moe_routing_out *routing, void *stream,
                              void *const *events)
 {
+    return moe::forward_impl(l, x, logits, shared, out, ws, ws_bytes, routing, stream, events,
+                             true);
+}
+
+}  // extern "C"
+
+// The forward's body.  may_prepare = false (the allocation-free entry):
+// a layer whose binding is not prepared yet is an error instead of a
+// prepare, which allocates.
+moe_status moe::forward_impl(const moe_layer *l, const moe_tensor *x, const moe_tensor *logits,
+                             const moe_tensor *shared, moe_tensor *out, void *ws,
+                             size_t ws_bytes, moe_routing_out *routing, void *stream,
+                             void *const *events, bool may_prepare)
+{
     if (!l || !x || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "NULL argument");
     moe_status st = check_bound(l);
     if (st) return st;
+    if (!may_prepare) {
+        std::lock_guard<std::mutex> lock(l->mu);
+        if (!l->prepared)
+            return fail(MOE_ERR_INVALID_ARGUMENT,
+                        "the layer is not prepared (call moe_prepare before an allocation-free "
+                        "forward: preparing allocates)");
+    }
     // no logits: the layer's bound router computes them
     // (absent means NULL or ndim 0: an empty [0, E] tensor may have no data)
     const bool own_router = !logits || logits->ndim == 0;
@@ -971,6 +995,13 @@ moe_status moe_forward_timed(const moe_layer *l, const moe_tensor *x, const moe_
     return copy_routing(l, T, wsb, W, routing, s);
 }
 
+moe_status moe::set_error(moe_status s, const char *msg)
+{
+    return fail(s, "%s", msg);
+}
+
+extern "C" {
+
 moe_status moe_router_logits(const moe_layer *l, const moe_tensor *x, moe_tensor *logits,
                              void *ws, size_t ws_bytes, void *stream)
 {
@@ -997,6 +1028,30 @@ moe_status moe_router_logits(const moe_layer *l, const moe_tensor *x, moe_tensor
     hipStream_t s = (hipStream_t)stream;
     if ((st = prepare_locked(l, s))) return st;
     return run_router(l, x->data, T, (float *)logits->data, (char *)ws, W, choose_path(l, T), s);
+}
+
+moe_status moe_borrowed_slots(const moe_layer *l, uint32_t *mask)
+{
+    if (!l || !mask) return fail(MOE_ERR_INVALID_ARGUMENT, "layer or mask is NULL");
+    std::lock_guard<std::mutex> lock(l->mu);
+    if (!l->bound) return fail(MOE_ERR_UNBOUND, "weights not bound (call moe_set_weights)");
+    const moe_tensor *slot[9] = {&l->w.gate_up_experts, &l->w.down_experts, &l->w.gate_experts,
+                                 &l->w.gate_up_bias, &l->w.down_bias, &l->w.gate_bias,
+                                 &l->w.e_score_correction_bias, &l->w.router_weight,
+                                 &l->w.router_bias};
+    uint32_t m = 0;
+    for (int i = 0; i < 9; ++i)
+        if (present(*slot[i])) m |= 1u << i;
+    if (l->prepared) {
+        // the GEMMs stream the library's packed MXFP4 copy of every expert
+        // stack, the fp16 copy of a 16-bit down stack, and the transposed router
+        if (l->wdtype == MOE_DTYPE_MXFP4)
+            m &= ~(MOE_SLOT_GATE_UP_EXPERTS | MOE_SLOT_DOWN_EXPERTS | MOE_SLOT_GATE_EXPERTS);
+        if (l->wdtype == MOE_DTYPE_BF16 && l->down_f16_ready) m &= ~MOE_SLOT_DOWN_EXPERTS;
+        if (l->wr_t) m &= ~MOE_SLOT_ROUTER_WEIGHT;
+    }
+    *mask = m;
+    return MOE_OK;
 }
 
 moe_status moe_destroy(moe_layer *l)

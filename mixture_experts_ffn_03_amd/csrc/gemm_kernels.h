@@ -13,15 +13,17 @@
 //         wave holds the gate and up accumulators of the same features in
 //         the same lanes, adds the biases and applies the gated activation.
 //         h is stored in fp16 (11-bit significand, 8x finer than bf16) when
-//         the whole tile fits fp16's range and the down weights convert
-//         exactly, else in bf16; one format byte per tile records the choice.
+//         the whole tile fits fp16's range and the down weights lie in it,
+//         else in bf16; one format byte per tile records the choice.
 //  act    (fc1 of a non-gated expert): the activation of every feature,
 //         stored like the gated h.
 //  down   (ONNX "MoE" fc2): when every h tile of its rows is fp16 (the
 //         normal case), a workgroup runs the f16 MFMA on the prepared fp16
 //         copy of the down weights, or, without one, converts the bf16 (or
-//         MXFP4) weights exactly to fp16 after their LDS read; otherwise it
-//         rounds the fp16 h fragments to bf16 and runs the bf16 MFMA.  Adds
+//         MXFP4) weights to fp16 after their LDS read (exact in fp16's
+//         normal range); otherwise it rounds the fp16 h fragments to bf16
+//         and runs the bf16 MFMA (on the fp16 copy rounded back to bf16 when
+//         the layer has one, so it never reads the caller's stack).  Adds
 //         the down bias and stores y (or, with a split reduction, each
 //         split's partial sums) per 64-feature chunk of a row: fp16 when the
 //         chunk fits fp16's range (half the bytes the combine reads back),
@@ -32,8 +34,10 @@
 // The token operand of the gated GEMM is gathered straight from x through the
 // permutation (row_token), so the permuted activations are never written.
 //
-// MXFP4 weights ("ClikaRT::nn::QMoEWoQ": weight-only, decoded one block at a
-// time inside the GEMM, never a dense copy): the packed codes and e8m0 scales
+// MXFP4 weights (the clika "ClikaRT::nn::QMoEWoQ" class description: the
+// experts are quantised, the activation is not, and the dequantisation
+// happens per block inside the product with no dense weight tensor in
+// memory): the packed codes and e8m0 scales
 // travel to LDS at 4.25 bits per weight; after the LDS read each lane turns
 // its 8 codes of a sub-step into 8 16-bit values with the gfx950 scaled
 // conversion (exact: e2m1 times a power of two fits bf16, and fp16 for the
@@ -58,7 +62,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -79,12 +82,14 @@ __device__ inline float e8m0_scale(uint32_t x)
     return __uint_as_float(x << 23);
 }
 
-// Two bf16 (low, high half of w) -> two fp16, exact for values in fp16's
-// normal range (the prepare-time range check guarantees it).
+// Two bf16 (low, high half of w) -> two fp16, rounded to nearest even like
+// the prepared fp16 copy (so both down paths compute on the same values):
+// exact in fp16's normal range, whose top the prepare-time range check
+// guarantees; a value below 2^-14 keeps the fewer bits of an fp16 subnormal
+// (absolute error at most 2^-25).
 __device__ inline uint32_t bf16x2_to_f16x2(uint32_t w)
 {
-    const fp16x2 p = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16),
-                                                __uint_as_float(w & 0xffff0000u));
+    const f16x2 p = {(_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xffff0000u)};
     return __builtin_bit_cast(uint32_t, p);
 }
 
@@ -130,7 +135,8 @@ __device__ inline f32x16 mfma(const u32x4 &a, const u32x4 &b, const f32x16 &c)
 // token lane % 32 of each 32x32 block.
 //  gated / act: (weigh-inputs: times the row's routing weight) + fc1 bias,
 //      activation, then h stored in fp16 when the tile's max |h| fits fp16
-//      and the down weights convert exactly, else bf16 (format byte per tile);
+//      and the down weights lie in fp16's range, else bf16 (format byte per
+//      tile);
 //  down / plain: + bias, f32 store.
 template <class TL, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
@@ -511,6 +517,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
             else chunks(std::false_type{});
             return;
         }
+        // plain (router logits [T, Nout], Nout = E of any size): a lane's 4
+        // features c .. c+3 go out as one 16-byte store when Nout is a
+        // multiple of 4 (every row then starts 16-byte aligned and a quad
+        // that starts inside the row ends inside it), else one by one up to
+        // Nout (a quad past the row's end would write into the next row, or
+        // past the buffer)
 #pragma unroll
         for (int f = 0; f < TL::FN; ++f)
 #pragma unroll
@@ -526,10 +538,16 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         float v = acc[f][m][i4 * 4 + j];
-                        if (bias) v += bias_at(bias, eb + c + j);
+                        if (bias && c + j < g.Nout) v += bias_at(bias, eb + c + j);
                         o[j] = v;
                     }
-                    *(f32x4 *)(yrow + c) = o;
+                    if ((g.Nout & 3) == 0) {
+                        *(f32x4 *)(yrow + c) = o;
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (c + j < g.Nout) yrow[c + j] = o[j];
+                    }
                 }
             }
     }
@@ -562,9 +580,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
 // 16-byte LDS read and lie in one scale block (h).
 //
 // Operand conversion happens after the LDS read, in registers: fp16 down GEMM
-// steps convert the bf16 weight fragments to fp16 (exact, range checked at
-// prepare) or decode MXFP4 to fp16; bf16 down GEMM steps round fp16-stored h
-// fragments to bf16.  Token chunks past the reduction length are read from a
+// steps convert the bf16 weight fragments to fp16 (exact in fp16's normal
+// range, whose top is checked at prepare) or decode MXFP4 to fp16; bf16 down
+// GEMM steps round fp16-stored h fragments to bf16 (and, on a layer with the
+// prepared fp16 copy, that copy's fragments back to bf16).  Token chunks past the reduction length are read from a
 // zero buffer; packed MXFP4 weights are zero past it already.
 
 template <int BN_, int BM_, int BK_, int WN_, int WM_, int SA_, int SB_, bool MX_, int WPE_ = 2>
@@ -675,9 +694,11 @@ __device__ const u32x4 g_zero16 = {0u, 0u, 0u, 0u};
 
 // RAGGED: the reduction length is not a multiple of BK (the last k-step's
 // token chunks past it read zeros); otherwise no k-step needs a bounds test.
-// WH (with F16, the down GEMM): the weights are the prepared fp16 copy
-// (g.w_f16), streamed as they are; otherwise F16 converts bf16 weight
-// fragments in registers.
+// WH (the down GEMM): the weights are the prepared fp16 copy (g.w_f16):
+// with F16 streamed as they are, without F16 (a bf16 down GEMM, some h tile
+// of its rows stored in bf16) each fragment rounded to bf16 after its LDS
+// read, so a layer with the copy never reads the caller's down stack.
+// Without WH, F16 converts bf16 weight fragments to fp16 in registers.
 template <class TL, int EPI, bool F16, bool RAGGED, bool WH = false>
 __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, uint8_t *lds,
                                          float *s_red)
@@ -734,7 +755,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
             const int f = min(tw.n0 + (up ? row - TL::BN / 2 : row), g.Nout - 1);
             const int64_t wrow = (int64_t)tw.e * g.w.e_rows + (int64_t)f * g.w.row_mul +
                                  (up ? g.w.off_up : g.w.off_gate);
-            const void *base = (F16 && WH) ? g.w_f16 : up ? g.w.w_up : g.w.w_gate;
+            const void *base = WH ? g.w_f16 : up ? g.w.w_up : g.w.w_gate;
             b_k[i] = c * 8;
             b_src[i] = (const uint8_t *)base + (wrow * Kd + c * 8) * 2;
         }
@@ -886,6 +907,9 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
                     if (F16 && !WH) {
 #pragma unroll
                         for (int w = 0; w < 4; ++w) bf[b][f][w] = bf16x2_to_f16x2(bf[b][f][w]);
+                    } else if (!F16 && WH) {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) bf[b][f][w] = f16x2_to_bf16x2(bf[b][f][w]);
                     }
                 }
             }
@@ -1006,6 +1030,9 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
                     if (F16 && !WH) {
 #pragma unroll
                         for (int w = 0; w < 4; ++w) bf[b][r][w] = bf16x2_to_f16x2(bf[b][r][w]);
+                    } else if (!F16 && WH) {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) bf[b][r][w] = f16x2_to_bf16x2(bf[b][r][w]);
                     }
                 }
             } else {
@@ -1154,6 +1181,10 @@ __global__ __launch_bounds__(TL::NT, TL::WPE) void gemm_dma_kernel(GemmArgs g)
                 if (ragged) dma_body<TL, EPI, true, true>(g, tw, lds, s_red);
                 else dma_body<TL, EPI, true, false>(g, tw, lds, s_red);
             }
+        } else if (!TL::MX && g.w_f16) {
+            // bf16 down GEMM of a layer with the fp16 copy: weights from the copy
+            if (ragged) dma_body<TL, EPI, false, true, true>(g, tw, lds, s_red);
+            else dma_body<TL, EPI, false, false, true>(g, tw, lds, s_red);
         } else {
             if (ragged) dma_body<TL, EPI, false, true>(g, tw, lds, s_red);
             else dma_body<TL, EPI, false, false>(g, tw, lds, s_red);

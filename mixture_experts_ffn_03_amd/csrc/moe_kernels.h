@@ -108,7 +108,7 @@ struct GemmArgs {
     int64_t yfmt_stride, yfmt_split_stride;
     int h_tiles;                 // GEMM-1 feature tiles (row stride of hfmt)
     int h_width;                 // h columns per GEMM-1 feature tile
-    int f16_ok;                  // the down weights convert exactly to fp16
+    int f16_ok;                  // the down weights lie in fp16's range
     // MXFP4 weights, packed once at prepare (see PackArgs): codes and scales
     // of logical row-block lb, k-step ks at pk + (lb-major) KiB blocks
     const uint8_t *pk;           // [E][nrb][nks][32 rows][32 bytes]

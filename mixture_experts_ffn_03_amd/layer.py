@@ -77,18 +77,36 @@ class MoE:
     def initialize(self, stream=None):
         _lib.check(_lib.lib().moe_prepare(self._h, C.c_void_p(_lib.stream_ptr(stream))))
 
+    def borrowed_slots(self) -> set:
+        """Names of the bound slots whose caller tensors a forward still reads
+        (moe_borrowed_slots); after initialize() the others may be released."""
+        m = C.c_uint32()
+        _lib.check(_lib.lib().moe_borrowed_slots(self._h, C.byref(m)))
+        return {k for k, bit in _lib.SLOT_BITS.items() if m.value & bit}
+
     # -- running ---------------------------------------------------------------
     def workspace_size(self, T: int) -> int:
         n = C.c_size_t()
         _lib.check(_lib.lib().moe_workspace_size(self._h, T, C.byref(n)))
         return n.value
 
-    def workspace(self, T: int, device) -> torch.Tensor:
-        """A cached byte workspace big enough for T tokens."""
+    def workspace(self, T: int, device, stream=None) -> torch.Tensor:
+        """A cached byte workspace big enough for T tokens, one per (device,
+        stream): allocated on the stream the library launches on, so the
+        caching allocator orders its reuse after that stream's kernels, and
+        calls on two streams never share one."""
         n = self.workspace_size(T)
-        if self._ws is None or self._ws.numel() < n or self._ws.device != torch.device(device):
-            self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
-        return self._ws
+        dev = torch.device(device)
+        s = torch.cuda.current_stream(dev) if stream is None else stream
+        key = (str(dev), s.cuda_stream)
+        if self._ws is None:
+            self._ws = {}
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < n:
+            with torch.cuda.stream(s):
+                ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+            self._ws[key] = ws
+        return ws
 
     @staticmethod
     def routing_buffers(T: int, E: int, K: int, device) -> dict:
@@ -117,8 +135,11 @@ class MoE:
         `events` (optional): MOE_STAGE_EVENTS raw hipEvent_t handles recorded
         at the stage boundaries (moe_forward_timed)."""
         T = x.numel() // x.shape[-1]
-        out = torch.empty_like(x) if out is None else out
-        ws = self.workspace(T, x.device) if workspace is None else workspace
+        if out is None:
+            with torch.cuda.stream(torch.cuda.current_stream(x.device) if stream is None
+                                   else stream):
+                out = torch.empty_like(x)
+        ws = self.workspace(T, x.device, stream) if workspace is None else workspace
         xt, lt, ot = _lib.tensor(x), _lib.tensor(router_logits), _lib.tensor(out)
         st = _lib.tensor(shared_output)
         r = self._routing_struct(routing)
@@ -138,9 +159,11 @@ class MoE:
                       stream=None) -> torch.Tensor:
         """x . Wr + Br (f32 [T, E]) from the bound router."""
         T = x.numel() // x.shape[-1]
-        out = torch.empty((T, self.E), dtype=torch.float32, device=x.device) \
-            if out is None else out
-        ws = self.workspace(T, x.device)
+        if out is None:
+            with torch.cuda.stream(torch.cuda.current_stream(x.device) if stream is None
+                                   else stream):
+                out = torch.empty((T, self.E), dtype=torch.float32, device=x.device)
+        ws = self.workspace(T, x.device, stream)
         xt, lt = _lib.tensor(x), _lib.tensor(out)
         _lib.check(_lib.lib().moe_router_logits(self._h, C.byref(xt), C.byref(lt),
                                                 C.c_void_p(ws.data_ptr()), ws.numel(),
@@ -151,8 +174,10 @@ class MoE:
               stream=None) -> dict:
         T = router_logits.numel() // router_logits.shape[-1]
         if routing is None:
-            routing = self.routing_buffers(T, self.E, self.K, router_logits.device)
-        ws = self.workspace(T, router_logits.device)
+            with torch.cuda.stream(torch.cuda.current_stream(router_logits.device)
+                                   if stream is None else stream):
+                routing = self.routing_buffers(T, self.E, self.K, router_logits.device)
+        ws = self.workspace(T, router_logits.device, stream)
         lt = _lib.tensor(router_logits)
         r = self._routing_struct(routing)
         _lib.check(_lib.lib().moe_route(self._h, C.byref(lt), C.byref(r),

@@ -110,7 +110,55 @@ def check_routing(cfg, inp: dict, r: dict, T: int):
 
 
 def sample_tokens(T: int, n: int, seed: int = 7) -> np.ndarray:
+    """Tokens 0, T // 2 and T - 1 plus n distinct random tokens (all of them
+    when n >= T), sorted."""
     rng = np.random.default_rng(seed)
-    base = {0, T - 1, T // 2}
+    base = {0, T - 1, T // 2} if T > 0 else set()
     base |= set(rng.choice(T, size=min(n, T), replace=False).tolist())
-    return np.array(sorted(base))[: max(n, 3)]
+    return np.array(sorted(base), dtype=np.int64)
+
+
+def tile_rows(counts: np.ndarray, bm: int):
+    """The grouped GEMMs' M-tiles: an expert with n >= bm rows has ceil(n/bm)
+    tiles over which its rows are spread evenly (tile t holds local rows
+    [t n / m, (t + 1) n / m)); one with 0 < n < bm rows has a single tile.
+    Yields (expert, first row, last row) in permutation row numbers."""
+    off = np.concatenate([[0], np.cumsum(counts)])
+    for e, n in enumerate(counts.tolist()):
+        if n == 0:
+            continue
+        m = -(-n // bm) if n >= bm else 1
+        for t in range(m):
+            r0, r1 = t * n // m, (t + 1) * n // m
+            if r1 > r0:
+                yield e, int(off[e] + r0), int(off[e] + r1 - 1)
+
+
+def covering_tokens(counts: np.ndarray, row_token: np.ndarray, bm: int, T: int,
+                    n_random: int = 0, seed: int = 7) -> np.ndarray:
+    """Tokens whose routed rows include the first and the last row of every
+    M-tile (so of every expert) of both grouped GEMMs, plus sample_tokens'
+    extremes and n_random random tokens.  Every output feature tile of such
+    a row is compared, so every (M-tile, N-tile) pair is checked at least
+    once."""
+    rows = set()
+    for _, r0, r1 in tile_rows(counts, bm):
+        rows.add(r0)
+        rows.add(r1)
+    toks = {int(row_token[r]) for r in rows}
+    toks |= set(sample_tokens(T, n_random, seed).tolist())
+    return np.array(sorted(toks), dtype=np.int64)
+
+
+def tile_height(cfg) -> int:
+    """Token-tile height the layer picks for this workload (its automatic
+    variant): 32-row tiles below 96 rows per expert, 128-row tiles for
+    MXFP4 below 512, else 256-row tiles; f32 layers use 32."""
+    if cfg.w_dtype == "f32":
+        return 32
+    rpe = cfg.T * cfg.K / cfg.E
+    if rpe < 96:
+        return 32
+    if cfg.w_dtype == "mxfp4" and rpe < 512:
+        return 128
+    return 256

@@ -130,3 +130,49 @@ def test_router_and_caller_logits_agree():
     b = layer(inp["x"], lg)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("E,K", [(6, 2), (2, 1), (10, 3)])
+def test_router_expert_count_not_multiple_of_four(E, K):
+    """Logit rows of E floats with E not a multiple of 4: the router GEMM's
+    stores stay inside each row and inside the buffer (a guard region after
+    the logits keeps its sentinel), the logits meet the f32 summation bound,
+    and the layer routed by its own router (whose logits sit in the workspace
+    just before the router's one-group tables) matches the oracle."""
+    T = 64
+    cfg = synth.MoeConfig(name="rt4", cid=305, T=T, H=256, I=128, E=E, K=K, router=True,
+                          bias_std=0.1, renormalize=True)
+    inp = synth.make_inputs(cfg, device=DEV)
+    del inp["logits"]
+    layer = from_config(cfg)
+    layer.set_weights_from(inp)
+    sentinel = 12345.0
+    buf = torch.full((T * E + 1024,), sentinel, dtype=torch.float32, device=DEV)
+    lg = buf[:T * E].view(T, E)
+    layer.router_logits(inp["x"], out=lg)
+    torch.cuda.synchronize()
+    assert (buf[T * E:] == sentinel).all(), "router GEMM wrote past the logits"
+    p = oracle.params_of(cfg)
+    ref = oracle.router_logits(p, host(inp))
+    bound = _logit_bound(inp, cfg.H)
+    err = np.abs(lg.double().cpu().numpy() - ref)
+    assert (err <= bound).all(), (err.max(), bound.min())
+
+    r = layer.routing_buffers(T, E, K, DEV)
+    out = layer(inp["x"], None, routing=r)
+    torch.cuda.synchronize()
+    ro = oracle.forward(p, host(inp), use_router=True)
+    ids = r["topk_ids"].cpu().numpy()
+    differ = (ids != ro["ids"]).any(1)
+    for t in np.nonzero(differ)[0]:
+        lf = ref[t].astype(np.float32).astype(np.float64)
+        kth = np.sort(lf)[::-1][K - 1]
+        near = set(np.nonzero(np.abs(lf - kth) <= 2 * bound[t])[0].tolist())
+        sym = set(ids[t].tolist()) ^ set(ro["ids"][t].tolist())
+        assert sym <= near, (t, ids[t], ro["ids"][t])
+    keep = ~differ
+    assert keep.sum() >= T - 1
+    counts = r["expert_counts"].cpu().numpy()
+    assert counts.sum() == T * K and (counts >= 0).all()
+    compare_out(out[torch.as_tensor(np.nonzero(keep)[0], device=out.device)],
+                ro["out"][keep], "bf16", f"router E={E}")

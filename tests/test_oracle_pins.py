@@ -393,6 +393,71 @@ def test_clamped_swiglu_reduces_to_silu_and_clamps(orc):
     assert abs(orc.activation(pl, 2.0, 0.5) - 2.0 * sig(3.404) * 1.5) < 1e-14
 
 
+def _swiglu(orc, alpha, beta, limit):
+    return _params(orc, 1, 2, 1, activation="swiglu_clamped", swiglu_alpha=alpha,
+                   swiglu_beta=beta, swiglu_limit=limit)
+
+
+def test_clamped_swiglu_gate_clamp_is_one_sided(orc):
+    """ONNX MoE `swiglu_limit` clamps the gate from above only: for a gate at
+    or past L the activation no longer moves, while below -L it still does
+    (a two-sided gate clamp would freeze it there too)."""
+    L = 7.0
+    p = _swiglu(orc, 1.702, 1.0, L)
+    for u in (-3.0, 0.25, 5.0):
+        top = [orc.activation(p, g, u) for g in (L, L + 0.5, 10.0, 1e3)]
+        assert len(set(top)) == 1, top
+        low = [orc.activation(p, g, u) for g in (-L - 0.5, -L - 1.0, -L - 2.0)]
+        assert len(set(low)) == 3 and all(v != top[0] for v in low), low
+    # the frozen value lies on the curve at g = L, where nothing is clamped
+    q = _swiglu(orc, 1.702, 1.0, 0.0)
+    assert orc.activation(p, 50.0, 0.25) == orc.activation(q, L, 0.25)
+
+
+def test_clamped_swiglu_up_clamp_is_two_sided(orc):
+    """The up projection is clamped to [-L, L]: the activation is flat in u
+    beyond either end, and the two flat values differ."""
+    L = 7.0
+    p = _swiglu(orc, 1.702, 1.0, L)
+    for g in (-2.0, 0.5, 3.0):
+        hi = {orc.activation(p, g, u) for u in (L, L + 1.0, 40.0)}
+        lo = {orc.activation(p, g, u) for u in (-L, -L - 1.0, -40.0)}
+        assert len(hi) == 1 and len(lo) == 1 and hi != lo, (hi, lo)
+        # inside the band the activation is strictly monotone in u
+        mid = [orc.activation(p, g, u) for u in (-6.0, -1.0, 0.0, 2.0, 6.5)]
+        d = np.diff(mid)
+        assert (d > 0).all() or (d < 0).all(), mid
+
+
+def test_clamped_swiglu_beta_added_after_the_clamp(orc):
+    """beta (ONNX MoE activation_beta) shifts the clamped up value: h is affine
+    in beta with slope h(g, 1; 0) - h(g, 0; 0) for every u, clamped or not (a
+    beta added before the clamp would leave a clamped u's h unmoved)."""
+    L = 7.0
+    for g in (-3.0, 0.75, 2.0, 9.0):
+        p0 = _swiglu(orc, 1.702, 0.0, L)
+        slope = orc.activation(p0, g, 1.0) - orc.activation(p0, g, 0.0)
+        assert slope != 0.0
+        for beta in (1.0, -0.5, 2.5):
+            pb = _swiglu(orc, 1.702, beta, L)
+            for u in (-40.0, -2.0, 0.0, 3.5, 40.0):
+                d = orc.activation(pb, g, u) - orc.activation(p0, g, u)
+                assert abs(d - beta * slope) <= 1e-12 * max(1.0, abs(beta * slope)), (g, beta, u)
+
+
+def test_clamped_swiglu_alpha_scales_the_sigmoid_argument(orc):
+    """alpha (ONNX MoE activation_alpha) sits inside the sigmoid: with no clamp
+    and beta 0, alpha = 0 gives h = g u / 2 exactly (sigmoid(0) = 1/2), a
+    large alpha gives g u for g > 0 and 0 for g < 0, and for g, u > 0 h grows
+    with alpha (an alpha outside the sigmoid would make h vanish at 0)."""
+    for g, u in ((1.5, 2.0), (-0.75, 3.0), (4.0, -1.25)):
+        assert orc.activation(_swiglu(orc, 0.0, 0.0, 0.0), g, u) == g * u / 2.0
+        big = orc.activation(_swiglu(orc, 200.0, 0.0, 0.0), g, u)
+        assert abs(big - (g * u if g > 0 else 0.0)) <= 1e-12 * abs(g * u)
+    hs = [orc.activation(_swiglu(orc, a, 0.0, 0.0), 1.5, 2.0) for a in (0.25, 0.5, 1.0, 1.702, 4.0)]
+    assert (np.diff(hs) > 0).all(), hs
+
+
 # --------------------------------------------------------------- MXFP4 pins
 
 def _load_e2m1():
@@ -490,6 +555,28 @@ def test_gelu_erf_tabulated(orc):
         # Phi(-v) = 1 - Phi(v)
         assert abs(orc.activation1(p, -v) - (-v) * (1.0 - phi)) < 1e-15 * max(1.0, v)
     assert orc.activation1(p, 0.0) == 0.0
+
+
+def test_gelu_tanh_constants(orc):
+    """The tanh form is v/2 (1 + tanh(c (v + a v^3))) with c = sqrt(2/pi) and
+    the published cubic coefficient a = 0.044715.  Inverting it at v = 1 and
+    v = 2 with the library atanh gives u(v) = c v (1 + a v^2) at two points,
+    which fixes c and a; a wrong constant in either place fails.  The
+    small-v limit (gelu(v) + gelu(-v)) / v^2 -> c pins c once more (it is
+    also the erf form's second-order Taylor term, 2 / sqrt(2 pi))."""
+    pt = _act_params(orc, "gelu", "tanh")
+    u1 = math.atanh(2.0 * orc.activation1(pt, 1.0) / 1.0 - 1.0)
+    u2 = math.atanh(2.0 * orc.activation1(pt, 2.0) / 2.0 - 1.0)
+    c = (4.0 * u1 - u2 / 2.0) / 3.0
+    a = (u2 / 2.0 - u1) / (3.0 * c)
+    assert abs(c - math.sqrt(2.0 / math.pi)) < 1e-12, c
+    assert abs(a - 0.044715) < 1e-11, a
+    v = 1e-4
+    lim = (orc.activation1(pt, v) + orc.activation1(pt, -v)) / (v * v)
+    assert abs(lim - 2.0 / math.sqrt(2.0 * math.pi)) < 1e-7, lim
+    pe = _act_params(orc, "gelu", "erf")
+    lim_e = (orc.activation1(pe, v) + orc.activation1(pe, -v)) / (v * v)
+    assert abs(lim_e - lim) < 1e-7
 
 
 def test_gelu_tanh_identities_and_distance(orc):
