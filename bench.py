@@ -15,10 +15,13 @@ it carries:
   - "workloads": the gpt-oss-20b-shaped MXFP4 layer and the DeepSeek-V3-shaped
     layer (and the decode step again), each with its own roofline object.
 Each of these is timed step by step with HIP events on the launch stream,
-with a >= 512 MiB scratch write between steps (outside the events) so that a
-step never finds the previous step's weights in the 256 MiB Infinity Cache.
-The headline's timed loop has no such write: its 2.8 GB of weights cycle the
-cache by themselves; its per-step flushed time is reported next to it.
+with a 1 GiB scratch buffer read between steps (outside the events) so that
+a step never finds the previous step's weights in the 256 MiB Infinity
+Cache.  The flush reads rather than writes: a write would leave the caches
+full of dirty lines whose write-back then competes with the measured step's
+weight stream (a serving step follows layers that read their weights).  The
+headline's timed loop has no flush: its 2.8 GB of weights cycle the cache by
+themselves; its per-step flushed time is reported next to it.
 
 The dominant kernel's duration is measured live with HIP events recorded by
 the library around each stage on the launch stream (moe_forward_timed).  The
@@ -41,7 +44,7 @@ METRIC = ("MoE layer active TFLOP/s + tokens/s (prefill); weight-stream HBM GB/s
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 STAGES = ["route", "permute", "gemm_gate_up", "gemm_down", "combine"]
-FLUSH_BYTES = 1 << 30       # scratch written between flushed steps (4x the MALL)
+FLUSH_BYTES = 1 << 30       # scratch read between flushed steps (4x the MALL)
 
 
 def log(*a):
@@ -239,16 +242,17 @@ def stage_times(hip, evs):
 
 
 def timed_flushed(wl, hip, steps: int, warmup: int, scratch):
-    """Step by step with a scratch write of FLUSH_BYTES before each step,
+    """Step by step with a read of the FLUSH_BYTES scratch before each step,
     outside the step's events.  Returns (mean ms, stage ms, min ms)."""
     import torch
+    words = scratch.view(torch.int32)
     for _ in range(warmup):
-        scratch.fill_(1)
+        words.max()
         wl.step()
     torch.cuda.synchronize()
     evs = [[hip.event() for _ in range(6)] for _ in range(steps)]
     for k in range(steps):
-        scratch.fill_(k & 0xff)
+        words.max()
         wl.step(events=evs[k])
     torch.cuda.synchronize()
     per = [hip.elapsed_ms(row[0], row[5]) for row in evs]
@@ -334,7 +338,7 @@ def main():
             hip.destroy(e)
     head = wl.summary(ms, stage_ms, flushed=False)
 
-    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    scratch = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     fl_ms, fl_st, fl_min = timed_flushed(wl, hip, min(args.steps, 10), 1, scratch)
     log(f"[bench] {cfg.name}: {ms:.4f} ms/step back to back, {fl_ms:.4f} flushed")
 
@@ -368,7 +372,7 @@ def main():
         "gemms_frac": head.get("gemms_frac"),
         "flushed": {"ms_per_step": fl_ms, "min_ms": fl_min,
                     "stages_ms": {k: round(v, 4) for k, v in fl_st.items()},
-                    "scratch_bytes": FLUSH_BYTES},
+                    "scratch_read_bytes": FLUSH_BYTES},
         "roofline": head["roofline"],
     }
     if not args.no_cpu_baseline:
