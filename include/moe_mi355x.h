@@ -294,6 +294,30 @@ moe_status moe_forward_timed(const moe_layer *layer, const moe_tensor *x,
                              moe_routing_out *routing, void *stream,
                              void *const *events);
 
+/* Bytes of the static per-GPU workspace of moe_forward_noalloc. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* moe_forward with no workspace argument and no device allocation, for the
+ * callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The workspace is a static array of
+ * MOE_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU it
+ * runs on until the process ends (the current device's copy is used).
+ * Arguments and results are those of moe_forward without the workspace.
+ *  - The layer must be prepared (moe_prepare, or one moe_forward since the
+ *    last moe_set_weights): preparing allocates, so an unprepared layer is an
+ *    INVALID_ARGUMENT error here.
+ *  - The call must fit: moe_workspace_size(T) <= MOE_NOALLOC_SCRATCH_BYTES,
+ *    else WORKSPACE (e.g. T = 32 at H 2048, I 768, E 128, K 8 needs < 3 MiB).
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents: calls that overlap in time on one GPU (two host threads,
+ *    or two streams with no ordering between them) race and give undefined
+ *    results.  Calls ordered on one stream are safe.
+ * Errors: as moe_forward. */
+moe_status moe_forward_noalloc(const moe_layer *layer, const moe_tensor *x,
+                               const moe_tensor *router_logits,
+                               const moe_tensor *shared_output, moe_tensor *out,
+                               moe_routing_out *routing, void *stream);
+
 /* Routing and permutation alone (the first two steps of moe_forward):
  * router_logits [T, E] f32 -> `routing` (non-NULL; any member may be NULL).
  * Needs moe_workspace_size(T) bytes of workspace. */

@@ -30,8 +30,9 @@ WDTYPE = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16, "mxfp4": MOE_DTYPE_MXFP4
 
 EXPORTS = ["moe_options_default", "moe_create", "moe_set_weights", "moe_prepare",
            "moe_workspace_size", "moe_forward", "moe_forward_timed", "moe_route",
-           "moe_router_logits", "moe_borrowed_slots", "moe_destroy", "moe_last_error",
-           "moe_status_string"]
+           "moe_router_logits", "moe_borrowed_slots", "moe_forward_noalloc", "moe_destroy",
+           "moe_last_error", "moe_status_string"]
+NOALLOC_SCRATCH_BYTES = 32 << 20
 # moe_borrowed_slots bits, one per moe_weights member in field order
 SLOT_BITS = {"gate_up_experts": 0x001, "down_experts": 0x002, "gate_experts": 0x004,
              "gate_up_bias": 0x008, "down_bias": 0x010, "gate_bias": 0x020,
@@ -105,6 +106,9 @@ def lib():
             "moe_router_logits": ([P, C.POINTER(moe_tensor), C.POINTER(moe_tensor), P,
                                    C.c_size_t, P], C.c_int),
             "moe_borrowed_slots": ([P, C.POINTER(C.c_uint32)], C.c_int),
+            "moe_forward_noalloc": ([P, C.POINTER(moe_tensor), C.POINTER(moe_tensor),
+                                     C.POINTER(moe_tensor), C.POINTER(moe_tensor),
+                                     C.POINTER(moe_routing_out), P], C.c_int),
             "moe_destroy": ([P], C.c_int),
             "moe_last_error": ([], C.c_char_p),
             "moe_status_string": ([C.c_int], C.c_char_p),

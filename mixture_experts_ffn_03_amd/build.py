@@ -23,7 +23,7 @@ ARCH = "gfx950"
 # compile in parallel
 SOURCES = ["gemm_prefill.hip", "gemm_prefill_mx.hip", "gemm_mid.hip", "gemm_decode.hip",
            "api.cpp", "route.hip", "permute.hip", "gemm.hip", "gemm_f32.hip",
-           "combine.hip", "router.hip"]
+           "combine.hip", "router.hip", "noalloc.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

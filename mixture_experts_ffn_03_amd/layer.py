@@ -155,6 +155,20 @@ class MoE:
 
     __call__ = forward
 
+    def forward_noalloc(self, x: torch.Tensor, router_logits: Optional[torch.Tensor],
+                        shared_output: Optional[torch.Tensor] = None, *, out: torch.Tensor,
+                        routing: Optional[dict] = None, stream=None):
+        """moe_forward_noalloc: the same step with the library's static per-GPU
+        workspace and no device allocation (the layer must be initialized and
+        `out` given)."""
+        xt, lt, ot = _lib.tensor(x), _lib.tensor(router_logits), _lib.tensor(out)
+        st = _lib.tensor(shared_output)
+        r = self._routing_struct(routing)
+        _lib.check(_lib.lib().moe_forward_noalloc(
+            self._h, C.byref(xt), C.byref(lt), C.byref(st), C.byref(ot),
+            C.byref(r) if r is not None else None, C.c_void_p(_lib.stream_ptr(stream))))
+        return out
+
     def router_logits(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
                       stream=None) -> torch.Tensor:
         """x . Wr + Br (f32 [T, E]) from the bound router."""
