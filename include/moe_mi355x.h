@@ -120,18 +120,29 @@ typedef struct moe_options {
                                      expert's weight scales the input it reads and
                                      its output joins the sum unweighted.  0 or 1;
                                      default 0                                      */
-    int32_t down_fp16_copy;       /* bf16 layers whose down weights lie in fp16's
-                                     range (checked by moe_prepare; the fp16 down
-                                     GEMM runs only then): 1 keeps a
-                                     library-owned fp16 copy of them (E*H*I*2 bytes
-                                     of device memory, made by moe_prepare, freed by
-                                     moe_destroy), so the fp16 down GEMM streams it
-                                     instead of converting each tile's weights in
-                                     registers, and the forward no longer reads the
-                                     caller's down stack, which the caller may then
-                                     release (moe_borrowed_slots): one resident
-                                     copy.  If the allocation fails the layer
-                                     converts per tile instead, without error.
+    int32_t down_fp16_copy;       /* bf16 layers with pack_weights whose down
+                                     weights lie in fp16's range (checked by
+                                     moe_prepare; the fp16 down GEMM runs only
+                                     then): 1 stores the prepared down copy in
+                                     fp16 (round to nearest even, exact in fp16's
+                                     normal range), so the fp16 down GEMM streams
+                                     it as it is; 0 keeps it bf16 and converts
+                                     each tile's weight fragments in registers.
+                                     0 or 1; default 1                              */
+    int32_t pack_weights;         /* bf16 layers: 1 makes moe_prepare copy the
+                                     gate||up (or fc1) and down stacks into
+                                     library-owned device memory (E*2I*H*2 +
+                                     E*H*I*2 bytes, rounded up to whole 256-row,
+                                     64-column tiles; freed by moe_destroy) in the
+                                     layout the GEMMs stream: per 256-row tile and
+                                     64-wide k-step one contiguous 32 KiB block
+                                     (the GEMMs then read weights from HBM at
+                                     ~6.1 TB/s instead of ~4.5 TB/s row by row).
+                                     The forward then reads no caller expert
+                                     stack, which the caller may release
+                                     (moe_borrowed_slots): one resident copy.  If
+                                     the allocation fails the layer streams the
+                                     caller's stacks instead, without error.
                                      0 or 1; default 1                              */
 } moe_options;
 
@@ -224,9 +235,9 @@ moe_status moe_set_weights(moe_layer *layer, const moe_weights *w);
  * declared slot is bound, scans the down weights for fp16's range (a 16-bit
  * down stack whose magnitudes stay within it converts exactly in fp16's
  * normal range; a value below 2^-14 keeps the fewer bits of an fp16
- * subnormal, an absolute error of at most 2^-25), packs MXFP4 stacks into
- * the layout the GEMMs stream, makes the fp16 down copy (down_fp16_copy)
- * and transposes a bound router.  Runs once per binding (a forward runs it
+ * subnormal, an absolute error of at most 2^-25), packs MXFP4 stacks and
+ * (pack_weights) 16-bit stacks into the layouts the GEMMs stream, and
+ * transposes a bound router.  Runs once per binding (a forward runs it
  * if needed) and synchronises `stream`.  Errors: UNBOUND, HIP. */
 moe_status moe_prepare(moe_layer *layer, void *stream);
 
@@ -249,15 +260,15 @@ moe_status moe_prepare(moe_layer *layer, void *stream);
  * borrowed.  After moe_prepare:
  *  - MXFP4 layers read only the library's packed copy of gate_up_experts,
  *    gate_experts and down_experts (codes and scales);
- *  - 16-bit layers whose prepare made the fp16 down copy (down weights in
- *    fp16's range, down_fp16_copy = 1, the allocation succeeded) read that
- *    copy instead of down_experts, including the bf16 fallback for h tiles
- *    beyond fp16's range;
+ *  - 16-bit layers whose prepare made the stage-layout copy (pack_weights
+ *    = 1 and the allocation succeeded) read it instead of gate_up_experts,
+ *    gate_experts and down_experts, including the bf16 fallback of the down
+ *    GEMM for h tiles beyond fp16's range;
  *  - a bound router is read from its transposed copy, not router_weight.
  * A slot whose bit is clear may be released or overwritten by the caller
  * until the next moe_set_weights (which drops the prepared state and makes
- * every slot borrowed again).  Biases and the gate||up stack of 16-bit layers
- * stay borrowed.  Errors: INVALID_ARGUMENT, UNBOUND. */
+ * every slot borrowed again).  Biases, the selection bias and f32 layers'
+ * stacks stay borrowed.  Errors: INVALID_ARGUMENT, UNBOUND. */
 moe_status moe_borrowed_slots(const moe_layer *layer, uint32_t *mask);
 
 /* Device workspace bytes a forward (or moe_route) on T tokens needs.  The

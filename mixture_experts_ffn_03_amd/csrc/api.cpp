@@ -38,11 +38,15 @@ struct moe_layer {
     // the bound router transposed to [E, H] (rows K-contiguous, like the
     // expert stacks) for the router GEMM; made at prepare, freed by destroy
     mutable void *wr_t = nullptr;
-    // options.down_fp16_copy: the bf16 down weights as fp16 [E, H, I],
-    // allocated at the first prepare that needs it, refilled by later ones;
-    // down_f16_ready says whether the current binding's copy is in it
-    mutable void *down_f16 = nullptr;
-    mutable bool down_f16_ready = false;
+    // options.pack_weights: the 16-bit expert stacks in the stage layout the
+    // GEMMs stream (Pack16Args): gate||up (or fc1) at pk16 + pk16_off[0], down
+    // at pk16 + pk16_off[1] (in fp16 when pk16_down_f16).  Allocated at the
+    // first prepare that needs it, refilled by later ones; pk16_ready says
+    // whether the current binding's copy is in it.
+    mutable uint8_t *pk16 = nullptr;
+    mutable int64_t pk16_off[2] = {0, 0};
+    mutable bool pk16_ready = false;
+    mutable bool pk16_down_f16 = false;
 };
 
 namespace {
@@ -145,6 +149,71 @@ moe_status check_bound(const moe_layer *l)
     return MOE_OK;
 }
 
+// Row mapping of the GEMM-1 weight operands (gate||up, or the fc1 stack of
+// a non-gated activation) and their biases.
+WeightRows gemm1_rows(const moe_layer *l)
+{
+    WeightRows w1{};
+    if (!gated(l)) {
+        // one fc1 stack [E, I, H] and its bias [E, I]
+        w1.w_gate = w1.w_up = l->w.gate_up_experts.data;
+        w1.s_gate = w1.s_up = l->w.gate_up_experts.scales;
+        w1.e_rows = l->I;
+        w1.row_mul = 1;
+        w1.off_gate = w1.off_up = 0;
+        if (present(l->w.gate_up_bias)) w1.b_gate = l->w.gate_up_bias.data;
+    } else if (fused(l)) {
+        w1.w_gate = w1.w_up = l->w.gate_up_experts.data;
+        w1.s_gate = w1.s_up = l->w.gate_up_experts.scales;
+        w1.e_rows = 2 * l->I;
+        if (l->opts.swiglu_fusion == MOE_FUSION_INTERLEAVED) {
+            w1.row_mul = 2;
+            w1.off_gate = 0;
+            w1.off_up = 1;
+        } else {
+            w1.row_mul = 1;
+            w1.off_gate = 0;
+            w1.off_up = (int)l->I;
+        }
+        if (present(l->w.gate_up_bias)) w1.b_gate = w1.b_up = l->w.gate_up_bias.data;
+    } else {
+        w1.w_gate = l->w.gate_experts.data;
+        w1.s_gate = l->w.gate_experts.scales;
+        w1.w_up = l->w.gate_up_experts.data;
+        w1.s_up = l->w.gate_up_experts.scales;
+        w1.e_rows = l->I;
+        w1.row_mul = 1;
+        w1.off_gate = w1.off_up = 0;
+        if (present(l->w.gate_bias)) w1.b_gate = l->w.gate_bias.data;
+        if (present(l->w.gate_up_bias)) w1.b_up = l->w.gate_up_bias.data;
+    }
+    return w1;
+}
+
+WeightRows down_rows(const moe_layer *l)
+{
+    WeightRows w2{};
+    w2.w_gate = w2.w_up = l->w.down_experts.data;
+    w2.s_gate = w2.s_up = l->w.down_experts.scales;
+    w2.e_rows = l->H;
+    w2.row_mul = 1;
+    if (present(l->w.down_bias)) w2.b_gate = l->w.down_bias.data;
+    return w2;
+}
+
+// Feature tiles of the two 16-bit GEMMs (every 16-bit tile family is
+// kPack16Rows weight rows wide: gate/up pairs of half that many features).
+int64_t gemm1_tiles(const moe_layer *l)
+{
+    const int64_t w = gated(l) ? kPack16Rows / 2 : kPack16Rows;
+    return (l->I + w - 1) / w;
+}
+
+int64_t gemm2_tiles(const moe_layer *l)
+{
+    return (l->H + kPack16Rows - 1) / kPack16Rows;
+}
+
 size_t align256(size_t v)
 {
     return (v + 255) & ~(size_t)255;
@@ -196,10 +265,18 @@ int path_bm(Path p)
     return gemm_bm(kind_of(p));
 }
 
-int path_bn(Path p, bool gated)
+// Output features per tile of GEMM 1 (gate/up pairs when gated) and of the
+// down GEMM on a path.
+int path_bn1(const moe_layer *l, Path p)
 {
-    if (p == Path::kF32) return gemm_f32_bn(gated);
-    return gemm_bn(kind_of(p), gated);
+    if (p == Path::kF32) return gemm_f32_bn(gated(l));
+    return gemm1_bn(kind_of(p), l->wdtype == MOE_DTYPE_MXFP4, gated(l));
+}
+
+int path_bn2(const moe_layer *l, Path p)
+{
+    if (p == Path::kF32) return gemm_f32_bn(false);
+    return gemm2_bn(kind_of(p), l->wdtype == MOE_DTYPE_MXFP4);
 }
 
 // Reduction splits of the down GEMM: its tile count (token tiles x feature
@@ -223,7 +300,7 @@ int down_splits(const moe_layer *l, int64_t T, Path path)
             cus = 256;
         }
     }
-    const int bm = path_bm(path), bn = path_bn(path, false);
+    const int bm = path_bm(path), bn = path_bn2(l, path);
     const int64_t tiles = max_m_tiles_of(l, T, bm) * ((l->H + bn - 1) / bn);
     if (tiles == 0 || tiles >= 3 * (int64_t)cus) return 1;
     const int64_t ksteps = (l->I + 63) / 64;
@@ -261,10 +338,11 @@ Workspace layout(const moe_layer *l, int64_t T)
     w.logits = take(T * l->E * 4);        // router logits when the layer's router runs
     w.router_grp = take(8 * 4);   // router GEMM: counts, offsets, tile_cum, full_cum
     // one h-format byte per (GEMM-1 M-tile, GEMM-1 feature tile), worst case
-    // over the two 16-bit kernel variants
+    // over the kernel variants
     size_t nfmt = 0;
     for (GemmKind k : {GemmKind::kPrefill, GemmKind::kDecode, GemmKind::kMid}) {
-        const int64_t ntile = (l->I + gemm_bn(k, true) - 1) / gemm_bn(k, true);
+        const int bn = gemm1_bn(k, l->wdtype == MOE_DTYPE_MXFP4, gated(l));
+        const int64_t ntile = (l->I + bn - 1) / bn;
         const size_t n = (size_t)(max_m_tiles_of(l, T, gemm_bm(k)) * ntile);
         if (n > nfmt) nfmt = n;
     }
@@ -368,7 +446,7 @@ moe_status run_router(const moe_layer *l, const void *x, int64_t T, float *logit
     // one group of T rows and few (E) features: the 32-row tiles give T / 32
     // workgroups where 256-row tiles would leave most CUs idle
     const Path rp = path == Path::kF32 ? Path::kF32 : Path::kDecode;
-    const int bm = path_bm(rp), bn = path_bn(rp, false);
+    const int bm = path_bm(rp), bn = rp == Path::kF32 ? gemm_f32_bn(false) : router_bn();
     g.nN = (int)((l->E + bn - 1) / bn);
     g.ksplit = 1;
     g.out = logits;
@@ -537,21 +615,50 @@ moe_status prepare_locked(const moe_layer *l, hipStream_t s)
         if ((st = hip_check(e, "prepare weight scan"))) return st;
         ok = mx ? (r[1] >= 104u && r[2] <= 140u) : (r[0] <= 0x477fu);
     }
-    l->down_f16_ready = false;
-    if (ok && l->wdtype == MOE_DTYPE_BF16 && l->opts.down_fp16_copy) {
-        const int64_t elems = l->E * l->H * l->I;
-        if (!l->down_f16 && hipMalloc(&l->down_f16, (size_t)elems * 2) != hipSuccess) {
-            (void)hipGetLastError();   // no room: the down GEMM converts per tile
-            l->down_f16 = nullptr;
+    l->pk16_ready = false;
+    l->pk16_down_f16 = false;
+    if (l->wdtype == MOE_DTYPE_BF16 && l->opts.pack_weights) {
+        const int64_t n1 = gemm1_tiles(l), n2 = gemm2_tiles(l);
+        const int64_t sz1 = pack16_bytes(l->E, n1, l->H), sz2 = pack16_bytes(l->E, n2, l->I);
+        if (!l->pk16) {
+            void *p = nullptr;
+            if (hipMalloc(&p, (size_t)(sz1 + sz2)) != hipSuccess) {
+                (void)hipGetLastError();   // no room: the GEMMs read the caller's rows
+                p = nullptr;
+            }
+            l->pk16 = (uint8_t *)p;
+            l->pk16_off[0] = 0;
+            l->pk16_off[1] = sz1;
         }
-        if (l->down_f16) {
-            // complete before prepare returns, like the rest of it (a forward on
-            // another stream may follow)
-            moe_status st = hip_check(launch_to_f16(l->w.down_experts.data, l->down_f16, elems, s),
-                                      "down weights to fp16");
-            if (!st) st = hip_check(hipStreamSynchronize(s), "prepare sync");
+        if (l->pk16) {
+            Pack16Args a{};
+            a.w = gemm1_rows(l);
+            a.gated = gated(l) ? 1 : 0;
+            a.Nout = (int)l->I;
+            a.K = (int)l->H;
+            a.E = (int)l->E;
+            a.nN = (int)n1;
+            a.nks = (int)((l->H + 63) / 64);
+            a.dst = l->pk16 + l->pk16_off[0];
+            moe_status st = hip_check(launch_pack16(a, s), "gate/up weight copy");
             if (st) return st;
-            l->down_f16_ready = true;
+            Pack16Args d{};
+            d.w = down_rows(l);
+            d.gated = 0;
+            d.Nout = (int)l->H;
+            d.K = (int)l->I;
+            d.E = (int)l->E;
+            d.nN = (int)n2;
+            d.nks = (int)((l->I + 63) / 64);
+            d.to_f16 = (ok && l->opts.down_fp16_copy) ? 1 : 0;
+            d.dst = l->pk16 + l->pk16_off[1];
+            if ((st = hip_check(launch_pack16(d, s), "down weight copy"))) return st;
+            // complete before prepare returns, like the rest of it (a forward
+            // on another stream may follow, and the caller may then release
+            // its stacks)
+            if ((st = hip_check(hipStreamSynchronize(s), "prepare sync"))) return st;
+            l->pk16_ready = true;
+            l->pk16_down_f16 = d.to_f16 != 0;
         }
     }
     if (l->wdtype == MOE_DTYPE_F32 && has_router(l)) {
@@ -584,6 +691,7 @@ moe_status moe_options_default(moe_options *o)
     o->swiglu_limit = 0.0f;
     o->gemm_variant = 0;
     o->down_fp16_copy = 1;
+    o->pack_weights = 1;
     return MOE_OK;
 }
 
@@ -633,6 +741,8 @@ moe_status moe_create(int64_t E, int64_t H, int64_t I, int64_t K, moe_dtype wdty
         return fail(MOE_ERR_INVALID_ARGUMENT, "weigh_inputs must be 0 or 1");
     if (o.down_fp16_copy != 0 && o.down_fp16_copy != 1)
         return fail(MOE_ERR_INVALID_ARGUMENT, "down_fp16_copy must be 0 or 1");
+    if (o.pack_weights != 0 && o.pack_weights != 1)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "pack_weights must be 0 or 1");
     if (o.swiglu_fusion < MOE_FUSION_NONE || o.swiglu_fusion > MOE_FUSION_SPLIT)
         return fail(MOE_ERR_INVALID_ARGUMENT, "unknown swiglu_fusion %d", o.swiglu_fusion);
     if (o.gemm_variant < 0 || o.gemm_variant > 3)
@@ -861,7 +971,7 @@ moe_status moe::forward_impl(const moe_layer *l, const moe_tensor *x, const moe_
     g1.Nout = (int)l->I;
     const bool gt = gated(l);
     const int epi1 = gt ? kEpiGated : kEpiAct;
-    const int bn1 = path_bn(path, gt);
+    const int bn1 = path_bn1(l, path);
     g1.nN = (int)((l->I + bn1 - 1) / bn1);
     g1.ksplit = 1;
     g1.out = wsb + W.h;
@@ -875,40 +985,7 @@ moe_status moe::forward_impl(const moe_layer *l, const moe_tensor *x, const moe_
     g1.h_tiles = g1.nN;
     g1.h_width = bn1;
     g1.f16_ok = l->down_f16_ok;
-    WeightRows &w1 = g1.w;
-    if (!gt) {
-        // one fc1 stack [E, I, H] and its bias [E, I]
-        w1.w_gate = w1.w_up = l->w.gate_up_experts.data;
-        w1.s_gate = w1.s_up = l->w.gate_up_experts.scales;
-        w1.e_rows = l->I;
-        w1.row_mul = 1;
-        w1.off_gate = w1.off_up = 0;
-        if (present(l->w.gate_up_bias)) w1.b_gate = l->w.gate_up_bias.data;
-    } else if (fz) {
-        w1.w_gate = w1.w_up = l->w.gate_up_experts.data;
-        w1.s_gate = w1.s_up = l->w.gate_up_experts.scales;
-        w1.e_rows = 2 * l->I;
-        if (l->opts.swiglu_fusion == MOE_FUSION_INTERLEAVED) {
-            w1.row_mul = 2;
-            w1.off_gate = 0;
-            w1.off_up = 1;
-        } else {
-            w1.row_mul = 1;
-            w1.off_gate = 0;
-            w1.off_up = (int)l->I;
-        }
-        if (present(l->w.gate_up_bias)) w1.b_gate = w1.b_up = l->w.gate_up_bias.data;
-    } else {
-        w1.w_gate = l->w.gate_experts.data;
-        w1.s_gate = l->w.gate_experts.scales;
-        w1.w_up = l->w.gate_up_experts.data;
-        w1.s_up = l->w.gate_up_experts.scales;
-        w1.e_rows = l->I;
-        w1.row_mul = 1;
-        w1.off_gate = w1.off_up = 0;
-        if (present(l->w.gate_bias)) w1.b_gate = l->w.gate_bias.data;
-        if (present(l->w.gate_up_bias)) w1.b_up = l->w.gate_up_bias.data;
-    }
+    g1.w = gemm1_rows(l);
 
     // GEMM 2: down + bias -> y (f32 space; in-range chunks stored in fp16 when yfmt is set)
     GemmArgs g2{};
@@ -921,19 +998,22 @@ moe_status moe::forward_impl(const moe_layer *l, const moe_tensor *x, const moe_
     g2.E = (int)l->E;
     g2.Kd = (int)l->I;
     g2.Nout = (int)l->H;
-    const int bn2 = path_bn(path, false);
+    const int bn2 = path_bn2(l, path);
     g2.nN = (int)((l->H + bn2 - 1) / bn2);
     g2.out = wsb + W.y;
     const int splits = down_splits(l, T, path);
     g2.ksplit = splits;
     g2.split_stride = T * l->K * l->H;
-    g2.w.w_gate = l->w.down_experts.data;
-    g2.w.s_gate = l->w.down_experts.scales;
-    g2.w.e_rows = l->H;
-    g2.w.row_mul = 1;
-    if (present(l->w.down_bias)) g2.w.b_gate = l->w.down_bias.data;
+    g2.w = down_rows(l);
     g2.hfmt = g1.hfmt;
-    if (l->down_f16_ready && path != Path::kF32) g2.w_f16 = l->down_f16;
+    if (l->pk16_ready && path != Path::kF32) {
+        // both GEMMs stream the prepared stage-layout copies
+        g1.wpk = l->pk16 + l->pk16_off[0];
+        g1.nks = (int)((l->H + 63) / 64);
+        g2.wpk = l->pk16 + l->pk16_off[1];
+        g2.nks = (int)((l->I + 63) / 64);
+        g2.wpk_f16 = l->pk16_down_f16 ? 1 : 0;
+    }
     g2.h_tiles = g1.nN;
     g2.h_width = bn1;
     g2.f16_ok = g1.f16_ok;
@@ -1043,11 +1123,12 @@ moe_status moe_borrowed_slots(const moe_layer *l, uint32_t *mask)
     for (int i = 0; i < 9; ++i)
         if (present(*slot[i])) m |= 1u << i;
     if (l->prepared) {
-        // the GEMMs stream the library's packed MXFP4 copy of every expert
-        // stack, the fp16 copy of a 16-bit down stack, and the transposed router
+        // the GEMMs stream the library's packed copy of every expert stack
+        // (MXFP4, or 16-bit in the stage layout), and the transposed router
         if (l->wdtype == MOE_DTYPE_MXFP4)
             m &= ~(MOE_SLOT_GATE_UP_EXPERTS | MOE_SLOT_DOWN_EXPERTS | MOE_SLOT_GATE_EXPERTS);
-        if (l->wdtype == MOE_DTYPE_BF16 && l->down_f16_ready) m &= ~MOE_SLOT_DOWN_EXPERTS;
+        if (l->wdtype == MOE_DTYPE_BF16 && l->pk16_ready)
+            m &= ~(MOE_SLOT_GATE_UP_EXPERTS | MOE_SLOT_DOWN_EXPERTS | MOE_SLOT_GATE_EXPERTS);
         if (l->wr_t) m &= ~MOE_SLOT_ROUTER_WEIGHT;
     }
     *mask = m;
@@ -1058,7 +1139,7 @@ moe_status moe_destroy(moe_layer *l)
 {
     if (l && l->mx_pack) (void)hipFree(l->mx_pack);
     if (l && l->wr_t) (void)hipFree(l->wr_t);
-    if (l && l->down_f16) (void)hipFree(l->down_f16);
+    if (l && l->pk16) (void)hipFree(l->pk16);
     delete l;
     return MOE_OK;
 }

@@ -1,5 +1,5 @@
 // Grouped expert GEMMs on gfx950 MFMA: the variant dispatcher and the
-// prepare-time kernels (fp16 copy, range scan, MXFP4 repack).  The GEMM
+// prepare-time kernels (16-bit stage-layout copy, range scan, MXFP4 repack).  The GEMM
 // kernels themselves are in gemm_kernels.h, instantiated per tile family in
 // gemm_prefill.hip, gemm_prefill_mx.hip, gemm_mid.hip and gemm_decode.hip.
 #include "gemm_kernels.h"
@@ -7,14 +7,35 @@
 namespace moe {
 namespace {
 
-// ---- prepare-time fp16 copy of a bf16 stack (round to nearest even; exact
-// for the stacks the range scan passes, save values below 2^-17, which keep
-// fewer bits as fp16 subnormals)
-__global__ __launch_bounds__(256) void to_f16_kernel(const uint16_t *src, _Float16 *dst, int64_t n)
+// ---- prepare-time copy of a 16-bit stack in the stage layout (Pack16Args).
+// Thread i writes 16-byte chunk i of the copy.
+__global__ __launch_bounds__(256) void pack16_kernel(Pack16Args a)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        dst[i] = (_Float16)bf16_bits_to_float(src[i]);
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = (int64_t)a.E * a.nN * a.nks * (kPack16Stage / 16);
+    if (i >= total) return;
+    const int q = (int)(i % (kPack16Stage / 16));
+    const int64_t blk = i / (kPack16Stage / 16);         // (e, nt, ks)
+    const int ks = (int)(blk % a.nks);
+    const int64_t ent = blk / a.nks;
+    const int nt = (int)(ent % a.nN), e = (int)(ent / a.nN);
+    const int row = q / 8, c = (q % 8) ^ ((row / 2) % 8);
+    const bool up = a.gated && row >= kPack16Rows / 2;
+    const int width = a.gated ? kPack16Rows / 2 : kPack16Rows;
+    const int f = nt * width + (up ? row - kPack16Rows / 2 : row);
+    const int k0 = ks * 64 + c * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (f < a.Nout && k0 < a.K) {
+        const int64_t wrow = (int64_t)e * a.w.e_rows + (int64_t)f * a.w.row_mul +
+                             (up ? a.w.off_up : a.w.off_gate);
+        const uint16_t *src = (const uint16_t *)(up ? a.w.w_up : a.w.w_gate) + wrow * a.K + k0;
+        v = *(const u32x4 *)src;
+        if (a.to_f16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = bf16x2_to_f16x2(v[j]);
+        }
+    }
+    *(u32x4 *)(a.dst + i * 16) = v;
 }
 
 // ---- prepare-time range scan of a down-weight stack
@@ -96,8 +117,16 @@ __global__ __launch_bounds__(256) void mx_pack_kernel(PackArgs a)
 static_assert(PrefillMXTile::BM == PrefillDTile::BM && PrefillMXTile::BN == PrefillDTile::BN, "");
 static_assert(DecodeMXTile::BM == DecodeDTile::BM && DecodeMXTile::BN == DecodeDTile::BN, "");
 static_assert(MidMXTile::BM == MidDTile::BM && MidMXTile::BN == MidDTile::BN, "");
+// Every 16-bit tile streams weight stages of the prepared copy's layout
+// (pack16_tile in gemm_kernels.h); the decode tiles assert it beside their
+// definitions.
+static_assert(pack16_tile<PrefillDTile>() && pack16_tile<PrefillFcTile>() &&
+                  pack16_tile<ShortFcTile>() && pack16_tile<DecodeDTile>() &&
+                  pack16_tile<MidDTile>(),
+              "tile and prepared weight layout agree");
 static_assert((PrefillDTile::BN / 2) % PrefillDTile::BK == 0 &&
-              (DecodeDTile::BN / 2) % DecodeDTile::BK == 0,
+              (DecodeDTile::BN / 2) % DecodeDTile::BK == 0 &&
+              (MidDTile::BN / 2) % MidDTile::BK == 0,
               "a down-GEMM k-step lies inside one h tile");
 
 int gemm_bm(GemmKind kind)
@@ -107,12 +136,26 @@ int gemm_bm(GemmKind kind)
                                       : DecodeDTile::BM;
 }
 
-int gemm_bn(GemmKind kind, bool gated)
+int gemm1_bn(GemmKind kind, bool mxfp4, bool gated)
 {
     const int bn = kind == GemmKind::kPrefill ? PrefillDTile::BN
                    : kind == GemmKind::kMid   ? MidDTile::BN
-                                              : DecodeDTile::BN;
+                   : mxfp4                    ? DecodeMXTile::BN
+                                              : decode16_bn1();
     return gated ? bn / 2 : bn;
+}
+
+int gemm2_bn(GemmKind kind, bool mxfp4)
+{
+    return kind == GemmKind::kPrefill ? PrefillDTile::BN
+           : kind == GemmKind::kMid   ? MidDTile::BN
+           : mxfp4                    ? DecodeMXTile::BN
+                                      : decode16_bn2();
+}
+
+int router_bn()
+{
+    return DecodeDTile::BN;
 }
 
 hipError_t launch_gemm_bf16(GemmKind kind, int epi, bool mxfp4, const GemmArgs &a,
@@ -140,9 +183,12 @@ hipError_t launch_mx_pack(const PackArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_to_f16(const void *src, void *dst, int64_t n, hipStream_t s)
+hipError_t launch_pack16(const Pack16Args &a, hipStream_t s)
 {
-    to_f16_kernel<<<4096, 256, 0, s>>>((const uint16_t *)src, (_Float16 *)dst, n);
+    const int64_t chunks = (int64_t)a.E * a.nN * a.nks * (kPack16Stage / 16);
+    const int64_t blocks = (chunks + 255) / 256;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    pack16_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -35,14 +35,19 @@ struct TileWork {
 // cut into 8 contiguous chunks, one per XCD (its L2 then serves the shared
 // panels and rows), and workgroup slot b / 8 walks its XCD's full chunk and
 // then its partial chunk.  The count of tiles is data dependent: the
-// prefix sums are staged in LDS, and surplus workgroups of the worst-case
-// grid return at once.
+// prefix sums, and the experts' row counts and offsets, are staged in LDS
+// together (one round trip to memory; s_cum holds 4 (E + 1) ints), and
+// surplus workgroups of the worst-case grid return at once.
 __device__ inline bool find_tile(const GemmArgs &g, int *s_cum, int n_width, TileWork *w)
 {
     int *s_full = s_cum + g.E + 1;
+    int *s_cnt = s_full + g.E + 1;
+    int *s_off = s_cnt + g.E + 1;
     for (int i = threadIdx.x; i <= g.E; i += blockDim.x) {
         s_cum[i] = g.tile_cum[i];
         s_full[i] = g.full_cum[i];
+        s_off[i] = g.offsets[i];
+        s_cnt[i] = i < g.E ? g.counts[i] : 0;
     }
     __syncthreads();
     // a split reduction multiplies the feature tiles: tile column
@@ -85,11 +90,11 @@ __device__ inline bool find_tile(const GemmArgs &g, int *s_cum, int n_width, Til
         return false;
     }
     // rows of M-tile mtile of the expert's ntl tiles
-    const int ntl = s_cum[e + 1] - s_cum[e], cnt = g.counts[e];
+    const int ntl = s_cum[e + 1] - s_cum[e], cnt = s_cnt[e];
     const int r0 = (int)((int64_t)mtile * cnt / ntl);
     const int r1 = (int)((int64_t)(mtile + 1) * cnt / ntl);
     w->e = e;
-    w->row0 = g.offsets[e] + r0;
+    w->row0 = s_off[e] + r0;
     w->nrows = r1 - r0;
     w->mg = s_cum[e] + mtile;
     w->ks = nt / g.nN;

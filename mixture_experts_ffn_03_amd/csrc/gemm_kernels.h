@@ -617,16 +617,29 @@ struct DTile {
                      : (NBC * NT == BN * CPR), "whole weight loads per thread");
     static_assert(NA >= 1 && NBC >= 1, "every thread loads A and B");
     static_assert(FN >= 2 && FN % 2 == 0, "gate/up pairs per wave");
-    static_assert(SA == 2 && SB >= SA && SB <= 4, "A one step ahead, B up to three");
+    // tokens one step ahead (SA = 2), or (the compiler-scheduled loop's deep
+    // mode) as many token stages as weight stages
+    static constexpr bool DEEP = SA == SB && SA > 2;
+    static_assert((SA == 2 || DEEP) && SB >= SA && SB <= 4, "A one or SB-1 steps ahead, B up to three");
     static_assert(2 * NB <= 63, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     static_assert(B_BYTES % 1024 == 0 || MX, "KiB-aligned stages");
-    static_assert(LDS_BYTES >= 2 * (kMaxExperts + 1) * 4 && LDS_BYTES >= NWAVES * 4,
+    static_assert(LDS_BYTES >= 4 * (kMaxExperts + 1) * 4 && LDS_BYTES >= NWAVES * 4,
                   "scheduling tables and epilogue scratch overlay the stages");
     // swizzle of token row r: rows r and r + 16/CPR start in the same bank group
     __device__ static inline int sw(int r) { return (r / (16 / CPR)) % CPR; }
     static_assert(CPR == 4 || CPR == 8 || CPR == 16, "row of 64, 128 or 256 bytes");
 };
+
+// A 16-bit tile reads weight stages from the prepared copy's blocks
+// (kPack16Rows rows of 64-wide k-steps, Pack16Args): its rows are a whole
+// block or an equal share of one, at 64-element k-steps of 128-byte rows.
+template <class TL>
+constexpr bool pack16_tile()
+{
+    return !TL::MX && TL::BK == 64 && TL::CPR == 8 && kPack16Rows % TL::BN == 0 &&
+           (TL::BN / 2) % 16 == 0;
+}
 
 // 512 threads, wave 64x128; k-steps of 64 (128-byte rows: a 64-byte row
 // piece halves the L2->LDS rate); A (token rows, L2/MALL resident) two
@@ -648,13 +661,20 @@ using ShortFcTile = DTile<256, 128, 64, 4, 1, 2, 4, false, 1>;
 static_assert(ShortFcTile::NT == PrefillFcTile::NT && ShortFcTile::WPE == PrefillFcTile::WPE &&
                   ShortFcTile::LDS_BYTES <= PrefillFcTile::LDS_BYTES,
               "the short body runs in the 256-row tile's workgroup and LDS");
-// 256 threads, wave 64x32; weights stream from HBM: four B stages.
-using DecodeDTile = DTile<256, 32, 64, 4, 1, 2, 4, false>;
+// 256 threads, wave 64x32; weights stream from HBM: four B stages, and four
+// token stages (4 KiB each, the loop's deep mode) so that two weight stages
+// stay in flight through each barrier and three between barriers.
+using DecodeDTile = DTile<256, 32, 64, 4, 1, 4, 4, false>;
 // The down GEMM at decode sizes has short reductions (I / 64 k-steps): two
 // B stages (72 KiB) let two workgroups share a CU, one streaming while the
 // other starts up (measured 0.081 -> 0.071 ms on the Qwen3-shaped step; the
 // gate||up GEMM, 32 k-steps per tile, keeps four stages).
 using DecodeDownTile = DTile<256, 32, 64, 4, 1, 2, 2, false>;
+// GEMM 1 at decode sizes: 128 weight rows (64 gate/up feature pairs), two
+// waves, four token and four weight stages of 16 KiB in 80 KiB, so that two
+// workgroups share a CU: one tile's start (its tile lookup, token rows and
+// first weight stages, a few microseconds) overlaps the other's stream.
+using DecodeFcTile = DTile<128, 32, 64, 2, 1, 4, 4, false>;
 // MXFP4 weights: a weight stage is 8.5 KiB, so four of them fit beside the
 // token stages (2 x 32 + 4 x 8.5 KiB; decode 2 x 4 + 4 x 8.5 KiB).
 using PrefillMXTile = DTile<256, 256, 64, 4, 2, 2, 4, true>;
@@ -694,11 +714,14 @@ __device__ const u32x4 g_zero16 = {0u, 0u, 0u, 0u};
 
 // RAGGED: the reduction length is not a multiple of BK (the last k-step's
 // token chunks past it read zeros); otherwise no k-step needs a bounds test.
-// WH (the down GEMM): the weights are the prepared fp16 copy (g.w_f16):
-// with F16 streamed as they are, without F16 (a bf16 down GEMM, some h tile
-// of its rows stored in bf16) each fragment rounded to bf16 after its LDS
-// read, so a layer with the copy never reads the caller's down stack.
-// Without WH, F16 converts bf16 weight fragments to fp16 in registers.
+// WH (the down GEMM): the weights are the prepared copy in fp16 (g.wpk with
+// g.wpk_f16): with F16 streamed as they are, without F16 (a bf16 down GEMM,
+// some h tile of its rows stored in bf16) each fragment rounded back to bf16
+// after its LDS read (exact: the copy came from bf16 values), so a layer with
+// the copy never reads the caller's down stack.  Without WH, F16 converts
+// bf16 weight fragments to fp16 in registers.  The weights come from the
+// prepared stage-layout copy whenever g.wpk is set, else from the caller's
+// rows.
 template <class TL, int EPI, bool F16, bool RAGGED, bool WH = false>
 __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, uint8_t *lds,
                                          float *s_red)
@@ -708,20 +731,20 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Kd = g.Kd;
 
-    // ---- per-load global sources of the token rows: row base + swizzled chunk
+    // ---- token rows of the per-load chunks (their global sources are set
+    // once the rows' token ids are known, below)
     const uint8_t *a_src[TL::NA];
     int a_k[TL::NA];                   // first k of the chunk this load fetches
     bool a_ok[TL::NA];                 // the chunk's row holds a token
+    int a_r[TL::NA];                   // its permutation row (clamped into the tile)
 #pragma unroll
     for (int i = 0; i < TL::NA; ++i) {
         const int q = (i * TL::NWAVES + wave) * 64 + lane;   // LDS chunk index
         const int row = q / TL::CPR, p = q % TL::CPR;
         const int c = p ^ TL::sw(row);
-        const int r = tw.row0 + min(row, tw.nrows - 1);
-        const int src = g.row_token ? g.row_token[r] : r;
+        a_r[i] = tw.row0 + min(row, tw.nrows - 1);
         a_k[i] = c * 8;
         a_ok[i] = row < tw.nrows;
-        a_src[i] = (const uint8_t *)g.a + ((int64_t)src * Kd + c * 8) * 2;
     }
     // ---- weight sources.  16-bit: row base + swizzled chunk.  MXFP4: this
     // lane's 16 bytes of the KiB code block of tile row-block t (load i), and
@@ -745,6 +768,29 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
         }
         const int t = wave * TL::RBW + min(lane / 4, TL::RBW - 1);
         s_src = g.pks + ((int64_t)tw.e * nrb_tot + lrb(t)) * g.nks * 64 + (lane % 4) * 16;
+    } else if (g.wpk) {
+        // the prepared stage-layout copy of kPack16Rows-row blocks: this
+        // load's 16 bytes of the tile's k-step block (LDS chunk q of the
+        // stage, the bank swizzle baked in).  A tile of fewer rows reads its
+        // share of a block -- for the gated GEMM its gate rows and its up
+        // rows -- whose rows start a multiple of 16 rows in, so they carry the
+        // same swizzle as in the tile's own stage.
+        constexpr int SUB = kPack16Rows / TL::BN;               // tiles per block
+        constexpr int FW = GATED ? kPack16Rows / 2 : kPack16Rows; // features per block
+        const int nblk = (g.Nout + FW - 1) / FW;
+        const int bi = tw.nt / SUB, h = tw.nt % SUB;
+        const uint8_t *blk = g.wpk + ((int64_t)tw.e * nblk + bi) * g.nks * kPack16Stage;
+#pragma unroll
+        for (int i = 0; i < TL::NBC; ++i) {
+            const int q = (i * TL::NWAVES + wave) * 64 + lane;
+            const int r = q / TL::CPR;
+            const int pr = GATED ? (r < TL::BN / 2 ? h * (TL::BN / 2) + r
+                                                   : kPack16Rows / 2 + h * (TL::BN / 2) +
+                                                         (r - TL::BN / 2))
+                                 : h * TL::BN + r;
+            b_k[i] = 0;
+            b_src[i] = blk + (pr * TL::CPR + q % TL::CPR) * 16;
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < TL::NBC; ++i) {
@@ -755,11 +801,16 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
             const int f = min(tw.n0 + (up ? row - TL::BN / 2 : row), g.Nout - 1);
             const int64_t wrow = (int64_t)tw.e * g.w.e_rows + (int64_t)f * g.w.row_mul +
                                  (up ? g.w.off_up : g.w.off_gate);
-            const void *base = WH ? g.w_f16 : up ? g.w.w_up : g.w.w_gate;
+            const void *base = up ? g.w.w_up : g.w.w_gate;
             b_k[i] = c * 8;
             b_src[i] = (const uint8_t *)base + (wrow * Kd + c * 8) * 2;
         }
     }
+    // bytes between a weight load's sources of consecutive k-steps, and
+    // whether a ragged last k-step selects zeros (the prepared copy is zero
+    // past the reduction length already)
+    const uint32_t b_step = (!TL::MX && g.wpk) ? (uint32_t)kPack16Stage : 2u * TL::BK;
+    const bool b_ragged = RAGGED && !(!TL::MX && g.wpk);
     const uint8_t *zero = (const uint8_t *)&g_zero16;
 
     // LDS byte offset of this wave's first KiB of a stage, and of its scale
@@ -799,10 +850,18 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
             const uint32_t st = wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
             const int k0 = kx(kt) * TL::BK;
             const bool full = kx(kt) < nfull;
-            dma16((!RAGGED || full || k0 + b_k[i] < Kd) ? b_src[i] + 2 * k0 : zero,
+            dma16((!b_ragged || full || k0 + b_k[i] < Kd) ? b_src[i] + (int64_t)kx(kt) * b_step
+                                                          : zero,
                   st + i * TL::NWAVES * 1024);
         }
     };
+    // the token rows' global sources (row_token: the gathered token of each row)
+#pragma unroll
+    for (int i = 0; i < TL::NA; ++i) {
+        const int src = g.row_token ? g.row_token[a_r[i]] : a_r[i];
+        a_src[i] = (const uint8_t *)g.a + ((int64_t)src * Kd + a_k[i]) * 2;
+    }
+
     // Branch-free forms for the interleaved loop.  A token row past the
     // tile fetches the 16 zero bytes at every step (its step is 0 bytes); a
     // step past the last one fetches the last step again (L2 hits) into its
@@ -834,8 +893,8 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
             }
         } else {
             const uint32_t st = wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
-            const uint8_t *p = b_src[i] + (uint64_t)kc * (2 * TL::BK);
-            if (RAGGED) p = ((int)kc * TL::BK + b_k[i] < Kd) ? p : zero;
+            const uint8_t *p = b_src[i] + (uint64_t)kc * b_step;
+            if (RAGGED && b_ragged) p = ((int)kc * TL::BK + b_k[i] < Kd) ? p : zero;
             dma16(p, st + i * TL::NWAVES * 1024);
         }
     };
@@ -940,42 +999,76 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
         // issue order, so A(j) and B(j) (issued before A(j)) are done once at
         // most the loads issued after A(j) are pending: B(j+SB-2) for j >= 1,
         // B(1..SB-2) for j = 0.
+        // Deep mode (SA = SB = S): the group after barrier j is A(j+S-1),
+        // B(j+S-1), prologue B(0), A(0), B(1), A(1), ..., B(S-2), A(S-2), so S-2 whole
+        // stages stay in flight through each barrier (with two token stages
+        // a barrier needs B(j+1) as well, which leaves one; a weight stream
+        // from HBM then stalls on latency).  Token loads of rows past the
+        // tile are skipped, so every wait counts weight loads only: at most
+        // c*NB pending, c the steps issued after the one needed, means that
+        // one is done (each later group holds NB weight loads).
         auto issue_group = [&](int j) {
-            if (j + 1 < nk) issue_a(j + 1);
-            if (j + TL::SB - 1 < nk) issue_b(j + TL::SB - 1);
+            if constexpr (TL::DEEP) {
+                if (j + TL::SB - 1 < nk) {
+                    issue_a(j + TL::SB - 1);
+                    issue_b(j + TL::SB - 1);
+                }
+            } else {
+                if (j + 1 < nk) issue_a(j + 1);
+                if (j + TL::SB - 1 < nk) issue_b(j + TL::SB - 1);
+            }
+        };
+        // wait until at most c steps' weight loads are pending, then barrier
+        auto wait_pending_steps = [&](int c) {
+            if (c >= 2) wait_loads_barrier<2 * TL::NB>();
+            else if (c == 1) wait_loads_barrier<TL::NB>();
+            else wait_loads_barrier<0>();
         };
         // the same group, load by load, spread over the sub-steps of step j
         // (a burst of DMA issues stalls the wave before its MFMAs); the
         // order of issue, which the waits rely on, is unchanged
         auto issue_group_part = [&](int j, int part) {
             constexpr int L = TL::NA + TL::NB;
+            const int ja = TL::DEEP ? j + TL::SB - 1 : j + 1;
 #pragma unroll
             for (int q = 0; q < L; ++q) {
                 if (q < part * L / NKS || q >= (part + 1) * L / NKS) continue;
                 if (q < TL::NA) {
-                    if (j + 1 < nk) issue_a_one(j + 1, q);
+                    if (ja < nk) issue_a_one(ja, q);
                 } else {
                     if (j + TL::SB - 1 < nk) issue_b_one(j + TL::SB - 1, q - TL::NA);
                 }
             }
         };
-        issue_b(0);
-        issue_a(0);
+        static_assert(TL::SB - 2 <= 2, "prologue wait cases");
+        if constexpr (TL::DEEP) {
+            issue_b(0);
+            issue_a(0);
 #pragma unroll
-        for (int s = 1; s < TL::SB - 1; ++s)
-            if (s < nk) issue_b(s);
-        {
-            const int after = min(TL::SB - 2, nk - 1);     // B steps issued after A(0)
-            if (after >= 2) wait_loads_barrier<2 * TL::NB>();
-            else if (after == 1) wait_loads_barrier<TL::NB>();
-            else wait_loads_barrier<0>();
-            static_assert(TL::SB - 2 <= 2, "prologue wait cases");
+            for (int s = 1; s < TL::SB - 1; ++s)
+                if (s < nk) {
+                    issue_b(s);
+                    issue_a(s);
+                }
+            wait_pending_steps(min(TL::SB - 2, nk - 1));   // steps issued after step 0
+        } else {
+            issue_b(0);
+            issue_a(0);
+#pragma unroll
+            for (int s = 1; s < TL::SB - 1; ++s)
+                if (s < nk) issue_b(s);
+            wait_pending_steps(min(TL::SB - 2, nk - 1));   // B steps issued after A(0)
         }
         issue_group(0);
         auto step_barrier = [&](int j) {
-            // (with SB = 2, B(j) follows A(j) in its group: wait for all)
-            if (TL::SB >= 3 && j + TL::SB - 2 < nk) wait_loads_barrier<TL::NB>();
-            else wait_loads_barrier<0>();
+            if constexpr (TL::DEEP) {
+                // steps j+1 .. j+S-2 issued after step j (those below nk)
+                wait_pending_steps(min(TL::SB - 2, nk - 1 - j));
+            } else {
+                // (with SB = 2, B(j) follows A(j) in its group: wait for all)
+                if (TL::SB >= 3 && j + TL::SB - 2 < nk) wait_loads_barrier<TL::NB>();
+                else wait_loads_barrier<0>();
+            }
         };
         read(0, 0, 0);
         for (int kt = 0; kt < nk; ++kt) {
@@ -1106,7 +1199,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     // every wave runs the same loads and barriers; only its MFMA work differs
     const int mv = min(max((tw.nrows - wm * TL::TM + 31) / 32, 0), TL::FM);
     if constexpr (TL::WPE == 1 || TL::MX) {
-        static_assert(TL::SB >= 3 && NKS >= 2, "interleaved loop");
+        static_assert(TL::SB >= 3 && NKS >= 2 && !TL::DEEP, "interleaved loop");
         // every count of 32-row blocks up to FM has its own loop
         static_assert(TL::FM <= 8, "block counts");
         switch (mv) {
@@ -1166,7 +1259,7 @@ __global__ __launch_bounds__(TL::NT, TL::WPE) void gemm_dma_kernel(GemmArgs g)
         __syncthreads();
         const bool f16 = *flag != 0;
         __syncthreads();                     // before the loads overwrite it
-        if (f16 && !TL::MX && g.w_f16) {
+        if (f16 && !TL::MX && g.wpk_f16) {
             if constexpr (std::is_same<TL, PrefillFcTile>::value) {
                 if (tw.nrows <= ShortFcTile::BM && !ragged) {
                     dma_body<ShortFcTile, EPI, true, false, true>(g, tw, lds, s_red);
@@ -1181,7 +1274,7 @@ __global__ __launch_bounds__(TL::NT, TL::WPE) void gemm_dma_kernel(GemmArgs g)
                 if (ragged) dma_body<TL, EPI, true, true>(g, tw, lds, s_red);
                 else dma_body<TL, EPI, true, false>(g, tw, lds, s_red);
             }
-        } else if (!TL::MX && g.w_f16) {
+        } else if (!TL::MX && g.wpk_f16) {
             // bf16 down GEMM of a layer with the fp16 copy: weights from the copy
             if (ragged) dma_body<TL, EPI, false, true, true>(g, tw, lds, s_red);
             else dma_body<TL, EPI, false, false, true>(g, tw, lds, s_red);

@@ -100,7 +100,13 @@ struct GemmArgs {
     // h storage formats, one byte per (GEMM-1 M-tile, GEMM-1 feature tile):
     // written by the gated GEMM, read per reduction step by the down GEMM.
     uint8_t *hfmt;
-    const void *w_f16;           // down GEMM: the prepared fp16 copy of w_gate, or null
+    // The prepared copy of the 16-bit weight stack in the stage layout the GEMM
+    // loads (see Pack16Args), or null: the kernel then reads w_gate / w_up
+    // row by row.  Tile (e, nt)'s k-step ks is one contiguous kPack16Stage-byte
+    // block at wpk + ((e * nN + nt) * nks + ks) * kPack16Stage.
+    const uint8_t *wpk;
+    int wpk_f16;                 // the prepared copy holds fp16 (the down GEMM's
+                                 // copy when the range scan allows), else bf16
     // down GEMM, or null (y in f32): per-chunk storage format of y (of each
     // split's partial sums), one byte per (split s, row r, kYWidth-feature
     // chunk q) at yfmt[s * yfmt_split_stride + r * yfmt_stride + q]
@@ -113,7 +119,8 @@ struct GemmArgs {
     // of logical row-block lb, k-step ks at pk + (lb-major) KiB blocks
     const uint8_t *pk;           // [E][nrb][nks][32 rows][32 bytes]
     const uint8_t *pks;          // [E][nrb][nks][2 scale blocks][32 rows]
-    int nks;                     // k-steps of 64 (the reduction length, rounded up)
+    int nks;                     // k-steps of 64 (the reduction length, rounded
+                                 // up): MXFP4 and prepared 16-bit copies
     int nrb_half;                // row-blocks of one operand (Nout / 32)
 };
 
@@ -151,9 +158,33 @@ inline int64_t mx_pack_scale_bytes(int ops, int64_t Nh, int64_t K, int64_t E)
     return E * (ops * Nh / 32) * ((K + 63) / 64) * 64;
 }
 
-// Prepare-time copy of a bf16 stack as fp16 (n elements; the stack passed
-// the fp16 range scan).
-hipError_t launch_to_f16(const void *src, void *dst, int64_t n, hipStream_t s);
+// Prepare-time copy of a 16-bit weight stack in the layout the grouped GEMMs
+// stream: per expert e, per tile of kPack16Rows weight rows (nt), per 64-wide
+// k-step ks, one block of kPack16Stage bytes that is the image of an LDS
+// weight stage -- 16-byte chunk q of the block holds row q / 8 of the tile,
+// columns 8 c .. 8 c + 7 of the k-step with c = (q % 8) ^ ((q / 8 / 2) % 8)
+// (the bank swizzle the GEMMs read with, applied once here).  Tile rows of
+// the gated GEMM are the tile's kPack16Rows / 2 gate features followed by
+// the same up features; other GEMMs take kPack16Rows consecutive features.
+// Rows past Nout and columns past K are zero.  A k-step of a tile is then
+// one contiguous read (a row-by-row read of 128 bytes per row streams
+// weights from HBM at 4.5 TB/s on MI355X, a contiguous one at 6.1).
+constexpr int kPack16Rows = 256;
+constexpr int kPack16Stage = kPack16Rows * 128;
+struct Pack16Args {
+    WeightRows w;                // source rows (w_gate / w_up, row mapping)
+    int gated;                   // tile rows are gate / up pairs of features
+    int Nout;                    // features (gate/up pairs when gated)
+    int K;                       // reduction length (multiple of 8)
+    int E, nN, nks;              // experts, tiles per expert, k-steps
+    int to_f16;                  // convert bf16 to fp16 (round to nearest even)
+    uint8_t *dst;
+};
+hipError_t launch_pack16(const Pack16Args &a, hipStream_t s);
+inline int64_t pack16_bytes(int64_t E, int64_t nN, int64_t K)
+{
+    return E * nN * ((K + 63) / 64) * kPack16Stage;
+}
 
 // Range of a down-weight stack, for the choice of the fp16 down GEMM:
 // out[0] = max over elements of the bf16 magnitude bits (0x7f80 = inf),
@@ -186,7 +217,14 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 // are read from the packed copy (GemmArgs pk / pks).
 enum class GemmKind { kPrefill = 0, kDecode = 1, kMid = 2 };
 int gemm_bm(GemmKind kind);          // token-tile height of a variant
-int gemm_bn(GemmKind kind, bool gated);   // output features per tile
+// output features per tile: GEMM 1 (gate||up or fc1; gate/up pairs when
+// gated), GEMM 2 (down), and the router GEMM
+int gemm1_bn(GemmKind kind, bool mxfp4, bool gated);
+int gemm2_bn(GemmKind kind, bool mxfp4);
+int router_bn();
+// the decode variant's 16-bit tiles (defined beside them, in gemm_decode.hip)
+int decode16_bn1();                  // weight rows of a GEMM-1 tile
+int decode16_bn2();
 hipError_t launch_gemm_bf16(GemmKind kind, int epi, bool mxfp4,
                             const GemmArgs &a, int64_t max_m_tiles, hipStream_t s);
 int gemm_f32_bm();

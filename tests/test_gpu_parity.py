@@ -164,7 +164,6 @@ def test_bf16_down_weight_beyond_fp16(variant):
     inp["down_experts"] = d
     ref = oracle_full(cfg, inp)["out"]
     out, r, layer = run_gpu(cfg, inp, gemm_variant=variant)
-    assert "down_experts" in layer.borrowed_slots()       # no fp16 copy was made
     check_routing(cfg, inp, r, cfg.T)
     cols = np.ones(cfg.H, bool)
     cols[5] = False
@@ -180,8 +179,8 @@ def test_released_stacks_after_prepare(name, variant):
     """One resident copy (the clika "ClikaRT::nn::QMoEWoQ" class description):
     after prepare, the expert stacks moe_borrowed_slots no longer lists are
     zero-filled by the caller, and the layer still matches the oracle run on
-    the original weights.  MXFP4 layers release every expert stack (codes and
-    scales), 16-bit layers the down stack (read from the fp16 copy)."""
+    the original weights.  MXFP4 layers (packed codes and scales) and 16-bit
+    layers (stage-layout copy) release every expert stack."""
     cfg = synth.CONFIGS[name]
     inp = synth.make_inputs(cfg, device=DEV)
     ref = oracle_full(cfg, inp)["out"]
@@ -193,10 +192,7 @@ def test_released_stacks_after_prepare(name, variant):
     kept = layer.borrowed_slots()
     stacks = {"gate_up_experts", "down_experts", "gate_experts"}
     released = {k for k in stacks if k in inp} - kept
-    if cfg.w_dtype == "mxfp4":
-        assert released == {k for k in stacks if k in inp}
-    else:
-        assert released == {"down_experts"}
+    assert released == {k for k in stacks if k in inp}
     for k in released:
         inp[k].zero_()
         if k.replace("experts", "scales") in inp:
@@ -306,13 +302,28 @@ def test_tile_row_splits(H, variant):
 
 @pytest.mark.parametrize("variant", [1, 2, 3])
 def test_down_weights_converted_per_tile(variant):
-    """down_fp16_copy = 0: the fp16 down GEMM converts its bf16 weight
-    fragments in registers (the default streams the prepared fp16 copy)."""
+    """down_fp16_copy = 0: the prepared down copy stays bf16 and the fp16 down
+    GEMM converts its weight fragments in registers (the default streams an
+    fp16 copy)."""
     cfg = synth.MIXTRAL_SMALL
     inp = synth.make_inputs(cfg, device=DEV)
     out, r, _ = run_gpu(cfg, inp, gemm_variant=variant, down_fp16_copy=0)
     check_routing(cfg, inp, r, cfg.T)
     compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"no fp16 copy variant {variant}")
+
+
+@pytest.mark.parametrize("name", ["mixtral_small", "qwen3_small", "deepseek_small"])
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_caller_stacks_unpacked(name, variant):
+    """pack_weights = 0: the GEMMs stream the caller's 16-bit stacks row by
+    row (no prepared copy); the down GEMM converts its weight fragments to
+    fp16 in registers."""
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, layer = run_gpu(cfg, inp, gemm_variant=variant, pack_weights=0)
+    assert {"gate_up_experts", "down_experts"} <= layer.borrowed_slots()
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"{name} unpacked v{variant}")
 
 
 @pytest.mark.parametrize("E,K", [(1, 1), (6, 6), (6, 1), (130, 7), (256, 64)])
