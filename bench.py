@@ -14,7 +14,9 @@ it carries:
     the weight-stream rate (touched experts' weight bytes per step);
   - "workloads": the gpt-oss-20b-shaped MXFP4 layer and the DeepSeek-V3-shaped
     layer (and the decode step again), each with its own roofline object.
-Each of these is timed step by step with HIP events on the launch stream,
+Each of these is timed step by step with HIP events on the launch stream
+(the step time from plain steps between two events, the stage times from a
+second pass with the library's stage events),
 with a 1 GiB scratch buffer read between steps (outside the events) so that
 a step never finds the previous step's weights in the 256 MiB Infinity
 Cache.  The flush reads rather than writes: a write would leave the caches
@@ -243,24 +245,37 @@ def stage_times(hip, evs):
 
 def timed_flushed(wl, hip, steps: int, warmup: int, scratch):
     """Step by step with a read of the FLUSH_BYTES scratch before each step,
-    outside the step's events.  Returns (mean ms, stage ms, min ms)."""
+    outside the step's timing.  Two passes: plain steps, each between two
+    events on the launch stream (the step time), then steps with the
+    library's stage events (stage times; on a step of a few tenths of a
+    millisecond the six extra event packets add about 3 us each).
+    Returns (mean ms, stage ms, min ms, mean ms of the staged pass)."""
     import torch
     words = scratch.view(torch.int32)
     for _ in range(warmup):
         words.max()
         wl.step()
     torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for k in range(steps):
+        words.max()
+        pairs[k][0].record()
+        wl.step()
+        pairs[k][1].record()
+    torch.cuda.synchronize()
+    plain = [a.elapsed_time(b) for a, b in pairs]
     evs = [[hip.event() for _ in range(6)] for _ in range(steps)]
     for k in range(steps):
         words.max()
         wl.step(events=evs[k])
     torch.cuda.synchronize()
-    per = [hip.elapsed_ms(row[0], row[5]) for row in evs]
+    staged = [hip.elapsed_ms(row[0], row[5]) for row in evs]
     st = stage_times(hip, evs)
     for row in evs:
         for e in row:
             hip.destroy(e)
-    return sum(per) / len(per), st, min(per)
+    return sum(plain) / len(plain), st, min(plain), sum(staged) / len(staged)
 
 
 def main():
@@ -339,7 +354,7 @@ def main():
     head = wl.summary(ms, stage_ms, flushed=False)
 
     scratch = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-    fl_ms, fl_st, fl_min = timed_flushed(wl, hip, min(args.steps, 10), 1, scratch)
+    fl_ms, fl_st, fl_min, fl_staged = timed_flushed(wl, hip, min(args.steps, 10), 1, scratch)
     log(f"[bench] {cfg.name}: {ms:.4f} ms/step back to back, {fl_ms:.4f} flushed")
 
     if wl.decode:
@@ -371,6 +386,7 @@ def main():
         "experts_touched": wl.touched,
         "gemms_frac": head.get("gemms_frac"),
         "flushed": {"ms_per_step": fl_ms, "min_ms": fl_min,
+                    "ms_per_step_with_stage_events": fl_staged,
                     "stages_ms": {k: round(v, 4) for k, v in fl_st.items()},
                     "scratch_read_bytes": FLUSH_BYTES},
         "roofline": head["roofline"],
@@ -390,9 +406,10 @@ def main():
             if name == headline:
                 continue
             sw = Workload(synth.CONFIGS[name], dev)
-            s_ms, s_st, s_min = timed_flushed(sw, hip, args.sub_steps, 2, scratch)
+            s_ms, s_st, s_min, s_staged = timed_flushed(sw, hip, args.sub_steps, 2, scratch)
             d = sw.summary(s_ms, s_st, flushed=True)
             d["min_ms"] = s_min
+            d["ms_per_step_with_stage_events"] = s_staged
             log(f"[bench] {name}: {s_ms:.4f} ms/step (flushed), gate||up "
                 f"{d['roofline']['frac']:.3f} of {d['roofline']['bound']} peak")
             subs[name] = d

@@ -75,11 +75,12 @@ __device__ inline float bias_at(const void *b, int64_t i)
 __device__ const uint16_t g_zero_bias[1] = {0};
 
 // e8m0 byte -> the fp32 multiplier 2^(X-127) (X = 0 is 2^-127, 255 is NaN).
+// Selects, not branches: in the k-loop a branch here put a wait for the
+// byte's LDS read, and the divergent-exec bookkeeping, between two MFMAs.
 __device__ inline float e8m0_scale(uint32_t x)
 {
-    if (x == 0u) return __uint_as_float(0x00400000u);
-    if (x == 255u) return __uint_as_float(0x7fc00000u);
-    return __uint_as_float(x << 23);
+    const uint32_t bits = x == 0u ? 0x00400000u : (x == 255u ? 0x7fc00000u : x << 23);
+    return __uint_as_float(bits);
 }
 
 // Two bf16 (low, high half of w) -> two fp16, rounded to nearest even like
@@ -1139,6 +1140,21 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
                 }
             }
         };
+        // MXFP4, next k-step: its code words and raw scale bytes are fetched
+        // right after the step barrier (all of them before any is used), and
+        // sub-step 0's fragments decoded only after the token reads, so the
+        // LDS round trip overlaps MFMAs instead of sitting between two
+        uint32_t sbyte[TL::MX ? TL::FN : 1];
+        auto mx_fetch = [&](int kt, int r) {
+            const uint8_t *sb = lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
+            const int t = brow(r) / 32;
+            cq[r] = *(const u32x4 *)(sb + t * 1024 + mx_code);
+            sbyte[r] = sb[TL::CODE_BYTES + t * 64 + mx_scale];
+        };
+        auto mx_decode0 = [&](int b, int r) {
+            scf[r] = e8m0_scale(sbyte[r]);
+            bf[b][r] = decode_mxfp4_8<F16>(cq[r][0], scf[r]);
+        };
         constexpr int NR = TL::FN + MV;                // reads per sub-step
         constexpr int L = TL::NA + TL::NB;             // loads per k-step
         constexpr int Q = TL::FN * MV;                 // MFMAs per sub-step
@@ -1193,11 +1209,31 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
                     fence();
                     // (past the last step these read a stale stage into the
                     // idle buffer: in bounds and never used)
+                    if constexpr (TL::MX) {
+                        // items: FN code/scale fetches, MV token reads, FN
+                        // decodes; two items per MFMA
+                        constexpr int NI = 2 * TL::FN + MV;
+                        constexpr int NM = Q - PRE;
+                        constexpr int IPM = NM > 0 ? (NI + NM - 1) / NM : NI;
 #pragma unroll
-                    for (int i = 0; i < (Q - PRE > NR ? Q - PRE : NR); ++i) {
-                        if (i < Q - PRE) mfma_q(cur, PRE + i);
-                        if (i < NR) read_one(kt + 1, 0, cur ^ 1, i);
-                        fence();
+                        for (int i = 0; i < (NM > NI ? NM : NI); ++i) {
+                            if (i < NM) mfma_q(cur, PRE + i);
+#pragma unroll
+                            for (int u = 0; u < IPM; ++u) {
+                                const int it = i * IPM + u;
+                                if (it < TL::FN) mx_fetch(kt + 1, it);
+                                else if (it < TL::FN + MV) read_one(kt + 1, 0, cur ^ 1, it);
+                                else if (it < NI) mx_decode0(cur ^ 1, it - TL::FN - MV);
+                            }
+                            fence();
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < (Q - PRE > NR ? Q - PRE : NR); ++i) {
+                            if (i < Q - PRE) mfma_q(cur, PRE + i);
+                            if (i < NR) read_one(kt + 1, 0, cur ^ 1, i);
+                            fence();
+                        }
                     }
                 }
             }
