@@ -1092,13 +1092,14 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     // The hand-laid k-loop (the 4-wave 16-bit tile, where one wave per SIMD
     // must keep the matrix pipe fed by itself, and the MXFP4 tiles, whose
     // decode work then sits between the MFMAs; each sched_barrier fences the
-    // compiler's scheduler).  In sub-steps 0 .. NKS-2 every MFMA is followed
-    // by one item: a fragment read of the next sub-step, then a DMA load of
-    // the step's group (A(kt+1), then B(kt+SB-1)), so the whole group goes
-    // out before the last sub-step.  The last sub-step issues half of its
-    // MFMAs, then the step barrier (its own fragments were read in the
-    // sub-step before), then the next step's reads between its remaining
-    // MFMAs.
+    // compiler's scheduler).  Every MFMA is followed by one item: a fragment
+    // read of the next sub-step, then a DMA load of a step's group (its A
+    // loads, then its B loads).  16-bit tiles put the step barrier at the end
+    // of sub-step 2 (below).  MXFP4 tiles issue the group of k-step kt --
+    // A(kt+1), B(kt+SB-1) -- over sub-steps 0 .. NKS-2; their last sub-step
+    // issues half of its MFMAs, then the step barrier (its own fragments
+    // were read in the sub-step before), then the next step's code fetches,
+    // token reads and decodes between its remaining MFMAs.
     auto kloop_il = [&](auto mv_tag) {
         constexpr int MV = decltype(mv_tag)::value;
         u32x4 bf[2][TL::FN], af[2][TL::FM > 0 ? TL::FM : 1];
@@ -1180,6 +1181,52 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
 #pragma unroll
         for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
         fence();
+        if constexpr (!TL::MX) {
+            // 16-bit weights.  The step barrier of k-step kt+1 closes sub-step
+            // 2 of k-step kt: by then every fragment of stage kt has been read
+            // (sub-step 3's in sub-step 2), so all 16 MFMAs of sub-step 3 can
+            // carry the reads of k-step kt+1's sub-step 0, and the group of
+            // loads that refills stage kt's slots -- A(kt+2), B(kt+SB) --
+            // starts right there: loads [0, P0) of group g in sub-step 3 of
+            // k-step g-1 (after the prologue for g = 0), [P0, P1) in sub-step
+            // 0 and [P1, L) in sub-step 1 of k-step g.  At the barrier of
+            // k-step kt+1 only the B loads of group kt are younger than
+            // A(kt+1), so a wait for at most NB pending loads covers A(kt+1)
+            // and B(kt+1).  (With the barrier inside sub-step 3, the next
+            // step's reads had only the MFMAs after it to hide behind.)
+            static_assert(NKS == 4, "four MFMA sub-steps per k-step");
+            constexpr int P0 = L * 3 / 8, P1 = P0 + (L - P0 + 1) / 2;
+#pragma unroll
+            for (int q = 0; q < P0; ++q) {
+                load_one(0, q);
+                fence();
+            }
+            for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int cur = ks & 1;
+                    const int lo = ks == 0 ? P0 : ks == 1 ? P1 : 0;
+                    const int hi = ks == 0 ? P1 : ks == 1 ? L : ks == 3 ? P0 : 0;
+                    const int g = ks == 3 ? kt + 1 : kt;
+                    const int rk = ks == 3 ? kt + 1 : kt, rs = ks == 3 ? 0 : ks + 1;
+                    constexpr int NI = NR + (P1 - P0 > P0 ? P1 - P0 : P0);
+#pragma unroll
+                    for (int i = 0; i < (Q > NI ? Q : NI); ++i) {
+                        if (i < Q) mfma_q(cur, i);
+                        // (past the last step the reads take a stale stage
+                        // into the idle buffer: in bounds and never used)
+                        if (i < NR) read_one(rk, rs, cur ^ 1, i);
+                        else if (i - NR < hi - lo) load_one(g, lo + i - NR);
+                        fence();
+                    }
+                    if (ks == NKS - 2 && kt + 1 < nk) {
+                        wait_loads_barrier<TL::NB>();
+                        fence();
+                    }
+                }
+            }
+            return;
+        }
         for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -1207,33 +1254,24 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
                     // A(kt+1) and B(kt+1) landed: only B(kt+SB-1) may be pending
                     if (kt + 1 < nk) wait_loads_barrier<TL::SB >= 3 ? TL::NB : 0>();
                     fence();
-                    // (past the last step these read a stale stage into the
-                    // idle buffer: in bounds and never used)
-                    if constexpr (TL::MX) {
-                        // items: FN code/scale fetches, MV token reads, FN
-                        // decodes; two items per MFMA
-                        constexpr int NI = 2 * TL::FN + MV;
-                        constexpr int NM = Q - PRE;
-                        constexpr int IPM = NM > 0 ? (NI + NM - 1) / NM : NI;
+                    // MXFP4 items: FN code/scale fetches, MV token reads, FN
+                    // decodes; two items per MFMA.  (Past the last step the
+                    // reads take a stale stage into the idle buffer: in bounds
+                    // and never used.)
+                    constexpr int NI = 2 * TL::FN + MV;
+                    constexpr int NM = Q - PRE;
+                    constexpr int IPM = NM > 0 ? (NI + NM - 1) / NM : NI;
 #pragma unroll
-                        for (int i = 0; i < (NM > NI ? NM : NI); ++i) {
-                            if (i < NM) mfma_q(cur, PRE + i);
+                    for (int i = 0; i < (NM > NI ? NM : NI); ++i) {
+                        if (i < NM) mfma_q(cur, PRE + i);
 #pragma unroll
-                            for (int u = 0; u < IPM; ++u) {
-                                const int it = i * IPM + u;
-                                if (it < TL::FN) mx_fetch(kt + 1, it);
-                                else if (it < TL::FN + MV) read_one(kt + 1, 0, cur ^ 1, it);
-                                else if (it < NI) mx_decode0(cur ^ 1, it - TL::FN - MV);
-                            }
-                            fence();
+                        for (int u = 0; u < IPM; ++u) {
+                            const int it = i * IPM + u;
+                            if (it < TL::FN) mx_fetch(kt + 1, it);
+                            else if (it < TL::FN + MV) read_one(kt + 1, 0, cur ^ 1, it);
+                            else if (it < NI) mx_decode0(cur ^ 1, it - TL::FN - MV);
                         }
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < (Q - PRE > NR ? Q - PRE : NR); ++i) {
-                            if (i < Q - PRE) mfma_q(cur, PRE + i);
-                            if (i < NR) read_one(kt + 1, 0, cur ^ 1, i);
-                            fence();
-                        }
+                        fence();
                     }
                 }
             }
