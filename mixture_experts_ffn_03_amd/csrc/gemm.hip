@@ -15,10 +15,10 @@ __global__ __launch_bounds__(256) void pack16_kernel(Pack16Args a)
     const int64_t total = (int64_t)a.E * a.nN * a.nks * (kPack16Stage / 16);
     if (i >= total) return;
     const int q = (int)(i % (kPack16Stage / 16));
-    const int64_t blk = i / (kPack16Stage / 16);         // (e, nt, ks)
-    const int ks = (int)(blk % a.nks);
-    const int64_t ent = blk / a.nks;
-    const int nt = (int)(ent % a.nN), e = (int)(ent / a.nN);
+    const int64_t blk = i / (kPack16Stage / 16);         // (e, ks, nt)
+    const int nt = (int)(blk % a.nN);
+    const int64_t eks = blk / a.nN;
+    const int ks = (int)(eks % a.nks), e = (int)(eks / a.nks);
     const int row = q / 8, c = (q % 8) ^ ((row / 2) % 8);
     const bool up = a.gated && row >= kPack16Rows / 2;
     const int width = a.gated ? kPack16Rows / 2 : kPack16Rows;

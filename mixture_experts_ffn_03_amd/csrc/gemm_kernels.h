@@ -750,6 +750,9 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     // ---- weight sources.  16-bit: row base + swizzled chunk.  MXFP4: this
     // lane's 16 bytes of the KiB code block of tile row-block t (load i), and
     // of the 64-byte scale piece of row-block RBW * wave + lane / 4.
+    // blocks per expert and k-step in the prepared 16-bit copy
+    const int pk_nblk = (g.Nout + (GATED ? kPack16Rows / 2 : kPack16Rows) - 1) /
+                        (GATED ? kPack16Rows / 2 : kPack16Rows);
     const uint8_t *b_src[TL::NBC];
     int b_k[TL::NBC];
     const uint8_t *s_src = nullptr;
@@ -771,16 +774,15 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
         s_src = g.pks + ((int64_t)tw.e * nrb_tot + lrb(t)) * g.nks * 64 + (lane % 4) * 16;
     } else if (g.wpk) {
         // the prepared stage-layout copy of kPack16Rows-row blocks: this
-        // load's 16 bytes of the tile's k-step block (LDS chunk q of the
-        // stage, the bank swizzle baked in).  A tile of fewer rows reads its
-        // share of a block -- for the gated GEMM its gate rows and its up
-        // rows -- whose rows start a multiple of 16 rows in, so they carry the
-        // same swizzle as in the tile's own stage.
+        // load's 16 bytes of the tile's block of k-step 0 (LDS chunk q of the
+        // stage, the bank swizzle baked in); a k-step moves on by the
+        // expert's nblk blocks.  A tile of fewer rows reads its share of a
+        // block -- for the gated GEMM its gate rows and its up rows -- whose
+        // rows start a multiple of 16 rows in, so they carry the same swizzle
+        // as in the tile's own stage.
         constexpr int SUB = kPack16Rows / TL::BN;               // tiles per block
-        constexpr int FW = GATED ? kPack16Rows / 2 : kPack16Rows; // features per block
-        const int nblk = (g.Nout + FW - 1) / FW;
         const int bi = tw.nt / SUB, h = tw.nt % SUB;
-        const uint8_t *blk = g.wpk + ((int64_t)tw.e * nblk + bi) * g.nks * kPack16Stage;
+        const uint8_t *blk = g.wpk + ((int64_t)tw.e * g.nks * pk_nblk + bi) * kPack16Stage;
 #pragma unroll
         for (int i = 0; i < TL::NBC; ++i) {
             const int q = (i * TL::NWAVES + wave) * 64 + lane;
@@ -810,7 +812,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     // bytes between a weight load's sources of consecutive k-steps, and
     // whether a ragged last k-step selects zeros (the prepared copy is zero
     // past the reduction length already)
-    const uint32_t b_step = (!TL::MX && g.wpk) ? (uint32_t)kPack16Stage : 2u * TL::BK;
+    const uint32_t b_step = (!TL::MX && g.wpk) ? (uint32_t)(pk_nblk * kPack16Stage) : 2u * TL::BK;
     const bool b_ragged = RAGGED && !(!TL::MX && g.wpk);
     const uint8_t *zero = (const uint8_t *)&g_zero16;
 
