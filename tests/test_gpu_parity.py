@@ -300,6 +300,26 @@ def test_tile_row_splits(H, variant):
     compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"rows H={H} variant {variant}")
 
 
+@pytest.mark.parametrize("H,I", [(200, 72), (1096, 776)])
+@pytest.mark.parametrize("act,layout", [("silu", "split"), ("swiglu_clamped", "interleaved"),
+                                        ("gelu", "split")])
+def test_decode_tiles_ragged_reduction(H, I, act, layout):
+    """The decode-sized tiles (32 token rows; weights from the prepared copy
+    with the non-temporal policy) with reductions that are not a multiple of
+    the 64-wide k-step in both GEMMs (the token chunks past H or I read as
+    zeros), expert biases, and up to about 40 rows per expert (one or two
+    32-row tiles each)."""
+    cfg = synth.MoeConfig(name="decr", cid=216, T=96, H=H, I=I, E=8, K=2,
+                          layout=layout, activation=act, expert_biases=True, bias_std=0.5,
+                          swiglu_alpha=1.702 if act == "swiglu_clamped" else 1.0,
+                          swiglu_beta=1.0 if act == "swiglu_clamped" else 0.0,
+                          swiglu_limit=7.0 if act == "swiglu_clamped" else 0.0)
+    inp = synth.make_inputs(cfg, device=DEV)
+    out, r, _ = run_gpu(cfg, inp, gemm_variant=2)
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], "bf16", f"decode ragged H={H} I={I} {act}")
+
+
 @pytest.mark.parametrize("variant", [1, 2, 3])
 def test_down_weights_converted_per_tile(variant):
     """down_fp16_copy = 0: the prepared down copy stays bf16 and the fp16 down
