@@ -29,7 +29,7 @@ import torch
 
 # tensor ids used in seeds
 T_X, T_LOGITS, T_GATE_UP, T_UP, T_DOWN, T_GU_BIAS, T_DOWN_BIAS, T_SEL_BIAS, \
-    T_GATE_BIAS, T_SHARED, T_ROUTER_W, T_ROUTER_B = range(12)
+    T_GATE_BIAS, T_SHARED, T_ROUTER_W, T_ROUTER_B, T_SHARED_GATE = range(13)
 
 # activations that read a gate and an up projection (the others read one)
 GATED_ACTS = ("silu", "swiglu_clamped")
@@ -61,6 +61,7 @@ class MoeConfig:
     selection_bias_std: Optional[float] = None   # e_score_correction_bias [E]
     logit_std: float = 1.0
     shared_output: bool = False   # draw a [T,H] shared-expert output
+    shared_gate: bool = False     # draw a shared-expert gate g [H] (x . g ~ N(0, 1))
     gelu_mode: str = "erf"        # "erf" | "tanh" (activation "gelu")
     weigh_inputs: bool = False    # kept weight scales the expert's input
     router: bool = False          # draw router_weight [H,E] and router_bias [E]
@@ -181,7 +182,8 @@ def make_inputs(cfg: MoeConfig, device="cpu", T: Optional[int] = None) -> dict:
     binds them: gate_up_experts, gate_experts (unfused only), down_experts,
     their ``*_scales`` for MXFP4, gate_up_bias / gate_bias / down_bias (when
     the workload has expert biases), e_score_correction_bias [E] f32 (when it
-    has a selection bias), shared_output [T,H] (when requested).
+    has a selection bias), shared_output [T,H] and shared_gate [H] (when
+    requested).
 
     Fused layouts put 2*I rows in gate_up_experts; for the unfused layout
     gate_up_experts holds the *up* rows [E,I,H] and gate_experts the gate rows.
@@ -227,6 +229,9 @@ def make_inputs(cfg: MoeConfig, device="cpu", T: Optional[int] = None) -> dict:
             seed_of(cid, T_SEL_BIAS))
     if cfg.shared_output:
         out["shared_output"] = normal((T, H), 1.0, xd, dev, seed_of(cid, T_SHARED))
+    if cfg.shared_gate:
+        out["shared_gate"] = normal((H,), 1.0 / math.sqrt(H), xd, dev,
+                                    seed_of(cid, T_SHARED_GATE))
     if cfg.router:
         # router Wr [H, E] (the layout of the MoeSpec router index arithmetic)
         out["router_weight"] = normal((H, E), 1.0 / math.sqrt(H), xd, dev,

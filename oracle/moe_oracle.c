@@ -435,9 +435,20 @@ static void token_forward(const orc_params *p, const orc_inputs *in, int64_t t,
         if (hdump) memcpy(hdump + j * I, hv, sizeof(double) * I);
         if (ydump) memcpy(ydump + j * H, yv, sizeof(double) * H);
     }
-    if (in->shared_output)
+    if (in->shared_output) {
+        /* logicaffeine "Moe" field `shared_gate`: the shared experts' output
+         * enters scaled by the logistic sigmoid of x . g (g a vector over the
+         * hidden features; the unscaled x, not a weigh-inputs copy) */
+        double sg = 1.0;
+        if (in->shared_gate) {
+            double d = 0.0;
+            for (int64_t c = 0; c < H; ++c)
+                d += x0[c] * elem(p->x_kind, in->shared_gate, c);
+            sg = 1.0 / (1.0 + exp(-d));
+        }
         for (int64_t c = 0; c < H; ++c)
-            out[c] += elem(p->x_kind, in->shared_output, t * H + c);
+            out[c] += sg * elem(p->x_kind, in->shared_output, t * H + c);
+    }
 }
 
 static void *worker(void *arg)

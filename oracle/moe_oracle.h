@@ -21,6 +21,7 @@
  *       the erf form (the pages name gelu_mode but print neither form).
  *   weigh-inputs routing                                          -- pinned
  *   router logits x . Wr + Br                                     -- pinned
+ *   shared-expert gate sigmoid(x . g) on the shared-output fold    -- pinned
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -72,6 +73,8 @@ typedef struct {
     const void *router_w;       /* [H,E] x_kind; when set, logits = x.Wr (+Br)
                                    and `logits` is not read                      */
     const void *router_b;       /* [E] x_kind; nullable                          */
+    const void *shared_gate;    /* [H] x_kind; nullable: with shared_output, the
+                                   fold is scaled by sigmoid(x . g)             */
 } orc_inputs;
 
 /* Routing for every token: ids [T,K] in rank order, weights [T,K] (fp64),

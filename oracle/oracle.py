@@ -41,7 +41,7 @@ class OrcInputs(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "x", "logits", "w_gu", "w_gu_scales", "w_gate", "w_gate_scales",
         "w_down", "w_down_scales", "b_gu", "b_gate", "b_down", "sel_bias",
-        "shared_output", "router_w", "router_b")]
+        "shared_output", "router_w", "router_b", "shared_gate")]
 
 
 def build(force: bool = False) -> str:
@@ -177,7 +177,8 @@ def _inputs(inp: dict, keep: dict, use_router: bool) -> OrcInputs:
         sel_bias=arr("e_score_correction_bias", np.float32),
         shared_output=arr("shared_output"),
         router_w=arr("router_weight") if use_router else None,
-        router_b=arr("router_bias") if use_router else None)
+        router_b=arr("router_bias") if use_router else None,
+        shared_gate=arr("shared_gate"))
 
 
 def router_logits(p: OrcParams, inp: dict) -> np.ndarray:

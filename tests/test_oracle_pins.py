@@ -267,6 +267,58 @@ def test_zero_down_weights_leave_the_weighted_bias(orc):
     np.testing.assert_allclose(r["out"], want, rtol=1e-14, atol=1e-15)
 
 
+def _gate_case(orc, weigh_inputs=False):
+    """A small f32 layer with a shared-expert output and a gate g whose dot
+    products with chosen tokens are 0, +40, -40 and three moderate values (g
+    is built from x by a numpy least-squares solve, so x . g is known
+    without the oracle)."""
+    cfg = synth.MoeConfig(name="sg", cid=105, T=24, H=32, I=12, E=5, K=2,
+                          x_dtype="f32", w_dtype="f32", shared_output=True,
+                          shared_gate=True, weigh_inputs=weigh_inputs)
+    inp = synth.make_inputs(cfg)
+    X = inp["x"].double().numpy()
+    # x . g = 0, +40, -40 on tokens 0-2 and moderate values on tokens 3-5;
+    # g stored as f32 (x . g then moves by ~1e-6)
+    g = np.linalg.lstsq(X[:6], np.array([0.0, 40.0, -40.0, 0.7, -1.3, 2.2]), rcond=None)[0]
+    g = g.astype(np.float32)
+    inp["shared_gate"] = torch.from_numpy(g)
+    p = orc.params_of(cfg)
+    gated = orc.forward(p, inp)["out"]
+    plain = orc.forward(p, {k: v for k, v in inp.items() if k != "shared_gate"})["out"]
+    routed = orc.forward(p, {k: v for k, v in inp.items()
+                             if k not in ("shared_gate", "shared_output")})["out"]
+    d = X @ g.astype(np.float64)
+    return inp, d, gated, plain, routed
+
+
+def test_shared_gate_is_the_logistic_of_x_dot_g(orc):
+    """logicaffeine "Moe" field `shared_gate`: the shared experts' output is
+    scaled by sigma(x . g).  Per token, (out - routed sum) / shared output is
+    the logistic function of the numpy dot product x . g: 1/2 where it is 0,
+    1 (the ungated fold) at +40, 0 (no shared term) at -40.  Fails a tanh or
+    exp(+d) form, a sign flip, or a gate applied to the routed sum."""
+    inp, d, gated, plain, routed = _gate_case(orc)
+    sh = inp["shared_output"].double().numpy()
+    want_gate = 1.0 / (1.0 + np.exp(-d))
+    assert abs(d[0]) < 1e-4 and abs(d[1] - 40) < 1e-4 and abs(d[2] + 40) < 1e-4
+    assert 0.05 < want_gate[3:6].min() and want_gate[3:6].max() < 0.95   # moderate gates
+    np.testing.assert_allclose(gated - routed, want_gate[:, None] * sh, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(gated[0] - routed[0], 0.5 * sh[0], rtol=1e-4, atol=1e-12)
+    np.testing.assert_allclose(gated[1], plain[1], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(gated[2], routed[2], rtol=1e-12, atol=1e-12)
+    # the routed part is untouched by the gate
+    assert np.abs(plain - routed - sh).max() <= 1e-12
+
+
+def test_shared_gate_reads_x_not_the_weighted_inputs(orc):
+    """With weigh-inputs routing (MoeSpec `weigh_inputs`) the experts read
+    w_j * x, but the shared gate is a function of the layer input x itself."""
+    inp, d, gated, plain, routed = _gate_case(orc, weigh_inputs=True)
+    sh = inp["shared_output"].double().numpy()
+    np.testing.assert_allclose(gated - routed, (1.0 / (1.0 + np.exp(-d)))[:, None] * sh,
+                               rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("layout", ["split", "interleaved", "unfused"])
 def test_dense_brute_force(orc, layout):
     """Evaluate every expert on every token densely (numpy matmul), then
