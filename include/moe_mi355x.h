@@ -176,7 +176,14 @@ typedef struct moe_tensor {
  *                    Binds whatever was declared, like the selection bias.
  *  router_bias     : optional router bias Br [E] (x dtype; MoeSpec
  *                    `router_bias`, added to each logit before scoring); needs
- *                    router_weight. */
+ *                    router_weight.
+ *  shared_gate     : optional shared-expert gate g [H] (x dtype; logicaffeine
+ *                    "Moe" field `shared_gate`: the shared experts' output is
+ *                    scaled by the logistic sigmoid of x . g).  When bound, a
+ *                    forward given shared_output adds sigmoid(x[t] . g) *
+ *                    shared_output[t] instead of shared_output[t] (x . g
+ *                    accumulated in f32); without shared_output it is not
+ *                    read.  Binds whatever was declared. */
 typedef struct moe_weights {
     moe_tensor gate_up_experts;
     moe_tensor down_experts;
@@ -187,6 +194,7 @@ typedef struct moe_weights {
     moe_tensor e_score_correction_bias;
     moe_tensor router_weight;
     moe_tensor router_bias;
+    moe_tensor shared_gate;
 } moe_weights;
 
 /* Optional copies of the routing state of a forward (all DEVICE pointers,
@@ -251,6 +259,7 @@ moe_status moe_prepare(moe_layer *layer, void *stream);
 #define MOE_SLOT_E_SCORE_CORRECTION_BIAS 0x040u
 #define MOE_SLOT_ROUTER_WEIGHT 0x080u
 #define MOE_SLOT_ROUTER_BIAS 0x100u
+#define MOE_SLOT_SHARED_GATE 0x200u
 
 /* Which bound caller buffers a forward still reads (the clika
  * "ClikaRT::nn::QMoEWoQ" class description: once packed, the layer keeps one

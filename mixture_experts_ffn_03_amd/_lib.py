@@ -36,7 +36,8 @@ NOALLOC_SCRATCH_BYTES = 32 << 20
 # moe_borrowed_slots bits, one per moe_weights member in field order
 SLOT_BITS = {"gate_up_experts": 0x001, "down_experts": 0x002, "gate_experts": 0x004,
              "gate_up_bias": 0x008, "down_bias": 0x010, "gate_bias": 0x020,
-             "e_score_correction_bias": 0x040, "router_weight": 0x080, "router_bias": 0x100}
+             "e_score_correction_bias": 0x040, "router_weight": 0x080, "router_bias": 0x100,
+             "shared_gate": 0x200}
 MOE_STAGE_EVENTS = 6
 
 
@@ -60,7 +61,7 @@ class moe_weights(C.Structure):
     _fields_ = [(n, moe_tensor) for n in (
         "gate_up_experts", "down_experts", "gate_experts", "gate_up_bias",
         "down_bias", "gate_bias", "e_score_correction_bias", "router_weight",
-        "router_bias")]
+        "router_bias", "shared_gate")]
 
 
 class moe_routing_out(C.Structure):

@@ -223,7 +223,7 @@ size_t align256(size_t v)
 struct Workspace {
     size_t ids, weights, block_counts, block_base, counts, offsets, tile_cum1, tile_cum2,
         full_cum1, full_cum2,
-        row_token, slot_row, row_weight, logits, router_grp, hfmt, h, y, yfmt, total;
+        row_token, slot_row, row_weight, logits, sgate, router_grp, hfmt, h, y, yfmt, total;
 };
 
 int64_t max_m_tiles_of(const moe_layer *l, int64_t T, int bm)
@@ -336,6 +336,7 @@ Workspace layout(const moe_layer *l, int64_t T)
     w.slot_row = take(TK * 4);
     w.row_weight = take(TK * 4);          // weigh-inputs: routing weight per row
     w.logits = take(T * l->E * 4);        // router logits when the layer's router runs
+    w.sgate = take(T * 4);                // shared-expert gate per token
     w.router_grp = take(8 * 4);   // router GEMM: counts, offsets, tile_cum, full_cum
     // one h-format byte per (GEMM-1 M-tile, GEMM-1 feature tile), worst case
     // over the kernel variants
@@ -378,9 +379,18 @@ int64_t tokens_of(const moe_tensor &t, int64_t last, bool *okp)
 
 // Routing + permutation into the workspace.
 moe_status run_route(const moe_layer *l, const float *logits, int64_t T, char *ws,
-                     const Workspace &W, Path path, hipStream_t s, void *const *events)
+                     const Workspace &W, Path path, hipStream_t s, void *const *events,
+                     const moe_tensor *x_gate = nullptr)
 {
     RouteArgs ra{};
+    if (x_gate) {
+        // the shared-expert gate of every token, from x and g
+        ra.x = x_gate->data;
+        ra.x_bf16 = x_gate->dtype == MOE_DTYPE_BF16;
+        ra.sgate = l->w.shared_gate.data;
+        ra.sgate_out = (float *)(ws + W.sgate);
+        ra.H = (int)l->H;
+    }
     ra.logits = logits;
     ra.sel_bias = present(l->w.e_score_correction_bias)
                       ? (const float *)l->w.e_score_correction_bias.data
@@ -820,6 +830,10 @@ moe_status moe_set_weights(moe_layer *l, const moe_weights *w)
             return fail(MOE_ERR_SHAPE_MISMATCH, "router_bias given without router_weight");
         if ((st = check_tensor("router_bias", w->router_bias, ad, {E}))) return st;
     }
+    // the shared-expert gate g [H] (logicaffeine "Moe" `shared_gate`)
+    if (present(w->shared_gate) &&
+        (st = check_tensor("shared_gate", w->shared_gate, ad, {H})))
+        return st;
     std::lock_guard<std::mutex> lock(l->mu);
     l->w = *w;
     l->bound = true;
@@ -951,12 +965,12 @@ moe_status moe::forward_impl(const moe_layer *l, const moe_tensor *x, const moe_
     const float *lg = own_router ? (const float *)(wsb + W.logits) : (const float *)logits->data;
     if (own_router && (st = run_router(l, x->data, T, (float *)(wsb + W.logits), wsb, W, path, s)))
         return st;
-    if ((st = run_route(l, lg, T, wsb, W, path, s, events))) return st;
+    const bool sgate = has_shared && present(l->w.shared_gate);
+    if ((st = run_route(l, lg, T, wsb, W, path, s, events, sgate ? x : nullptr))) return st;
 
     const int bm = path_bm(path);
     const int64_t max_m_tiles = max_m_tiles_of(l, T, bm);
     const bool mx = l->wdtype == MOE_DTYPE_MXFP4;
-    const bool fz = fused(l);
 
     // GEMM 1: gate||up with the fused activation -> h
     GemmArgs g1{};
@@ -1059,6 +1073,7 @@ moe_status moe::forward_impl(const moe_layer *l, const moe_tensor *x, const moe_
     ca.weights = (const float *)(wsb + W.weights);
     ca.slot_row = (const int32_t *)(wsb + W.slot_row);
     ca.shared = has_shared ? shared->data : nullptr;
+    ca.shared_scale = sgate ? (const float *)(wsb + W.sgate) : nullptr;
     ca.out = (void *)out->data;
     ca.T = (int)T;
     ca.H = (int)l->H;
@@ -1115,12 +1130,12 @@ moe_status moe_borrowed_slots(const moe_layer *l, uint32_t *mask)
     if (!l || !mask) return fail(MOE_ERR_INVALID_ARGUMENT, "layer or mask is NULL");
     std::lock_guard<std::mutex> lock(l->mu);
     if (!l->bound) return fail(MOE_ERR_UNBOUND, "weights not bound (call moe_set_weights)");
-    const moe_tensor *slot[9] = {&l->w.gate_up_experts, &l->w.down_experts, &l->w.gate_experts,
-                                 &l->w.gate_up_bias, &l->w.down_bias, &l->w.gate_bias,
-                                 &l->w.e_score_correction_bias, &l->w.router_weight,
-                                 &l->w.router_bias};
+    const moe_tensor *slot[10] = {&l->w.gate_up_experts, &l->w.down_experts, &l->w.gate_experts,
+                                  &l->w.gate_up_bias, &l->w.down_bias, &l->w.gate_bias,
+                                  &l->w.e_score_correction_bias, &l->w.router_weight,
+                                  &l->w.router_bias, &l->w.shared_gate};
     uint32_t m = 0;
-    for (int i = 0; i < 9; ++i)
+    for (int i = 0; i < 10; ++i)
         if (present(*slot[i])) m |= 1u << i;
     if (l->prepared) {
         // the GEMMs stream the library's packed copy of every expert stack

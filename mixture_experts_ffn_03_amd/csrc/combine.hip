@@ -4,7 +4,9 @@
 // ("MoeSpec" `weigh_inputs`) the weights were applied to the experts' inputs
 // and every kept output joins the sum with weight one.
 //
-// out[t, :] = sum_{j=0..K-1} w[t, j] * y[slot_row[t, j], :]  (+ shared[t, :])
+// out[t, :] = sum_{j=0..K-1} w[t, j] * y[slot_row[t, j], :]  (+ s[t] shared[t, :])
+// with s[t] = sigmoid(x[t] . g) when the layer's shared-expert gate is bound
+// (logicaffeine "Moe" `shared_gate`; computed by the route kernel), else 1.
 // accumulated in f32 in slot order j = 0, 1, ..., rounded once to the output
 // dtype (round to nearest even for bf16).  No atomics: each output element
 // is produced by one thread, so results are bitwise reproducible.  A chunk
@@ -93,8 +95,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     if (a.out_bf16) {
         if (a.shared) {
             const bf16x8 sh = *(const bf16x8 *)((const __bf16 *)a.shared + o);
+            const float sc = a.shared_scale ? a.shared_scale[t] : 1.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += (float)sh[e];
+            for (int e = 0; e < 8; ++e) acc[e] += sc * (float)sh[e];
         }
         bf16x8 r;
 #pragma unroll
@@ -104,8 +107,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
         float *out = (float *)a.out + o;
         if (a.shared) {
             const float *sh = (const float *)a.shared + o;
+            const float sc = a.shared_scale ? a.shared_scale[t] : 1.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += sh[e];
+            for (int e = 0; e < 8; ++e) acc[e] += sc * sh[e];
         }
         *(f32x4 *)out = f32x4{acc[0], acc[1], acc[2], acc[3]};
         *(f32x4 *)(out + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};

@@ -24,6 +24,13 @@ struct RouteArgs {
     int renormalize;
     int n_group, topk_group;
     float scale;             // routed scaling factor
+    // shared-expert gate (logicaffeine "Moe" `shared_gate`), or sgate null:
+    // sgate_out[t] = sigmoid(x[t] . g), x [T, H] and g [H] in x's dtype
+    const void *x;
+    const void *sgate;
+    float *sgate_out;
+    int H;
+    int x_bf16;
 };
 
 struct PermuteArgs {
@@ -200,6 +207,7 @@ struct CombineArgs {
     const float *weights;        // [T, K]
     const int32_t *slot_row;     // [T, K]
     const void *shared;          // [T, H] x dtype or null
+    const float *shared_scale;   // [T] scale of token t's shared output, or null (1)
     void *out;                   // [T, H] x dtype
     int T, H, K;
     int out_bf16;                // 1: bf16 x/out, 0: f32

@@ -153,6 +153,12 @@ __device__ inline double wave_sum(double v)
 
 constexpr int kNone = 0x7fffffff;
 
+// bf16 bits -> f32 (exact)
+__device__ inline float bf16_to_float(uint16_t b)
+{
+    return __uint_as_float((uint32_t)b << 16);
+}
+
 template <int EPL>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
 {
@@ -313,6 +319,25 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
     if (lane < a.K) {
         a.ids[(int64_t)t * a.K + lane] = my_id;
         a.weights[(int64_t)t * a.K + lane] = (float)my_w;
+    }
+
+    // shared-expert gate of token t (logicaffeine "Moe" `shared_gate`):
+    // sigmoid(x[t] . g), the dot product over the hidden features, lane l
+    // taking features l, l + 64, ... (coalesced), summed in fp64
+    if (a.sgate) {
+        double d = 0.0;
+        if (a.x_bf16) {
+            const uint16_t *xr = (const uint16_t *)a.x + (int64_t)t * a.H;
+            const uint16_t *gr = (const uint16_t *)a.sgate;
+            for (int c = lane; c < a.H; c += 64)
+                d += (double)bf16_to_float(xr[c]) * (double)bf16_to_float(gr[c]);
+        } else {
+            const float *xr = (const float *)a.x + (int64_t)t * a.H;
+            const float *gr = (const float *)a.sgate;
+            for (int c = lane; c < a.H; c += 64) d += (double)xr[c] * (double)gr[c];
+        }
+        d = wave_sum(d);
+        if (lane == 0) a.sgate_out[t] = (float)(1.0 / (1.0 + exp(-d)));
     }
 }
 

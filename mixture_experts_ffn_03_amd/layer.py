@@ -42,10 +42,11 @@ class MoE:
                     down_bias=None, gate_experts=None, gate_bias=None,
                     e_score_correction_bias=None, gate_up_scales=None,
                     down_scales=None, gate_scales=None, router_weight=None,
-                    router_bias=None):
+                    router_bias=None, shared_gate=None):
         """Bind the slots (device tensors, borrowed).  MXFP4 stacks are given as
         codes with their ``*_scales``.  router_weight [H, E] / router_bias [E]
-        (optional) let forward compute the router logits itself."""
+        (optional) let forward compute the router logits itself; shared_gate
+        [H] (optional) scales a given shared output by sigmoid(x . g)."""
         w = _lib.moe_weights()
         w.gate_up_experts = _lib.tensor(gate_up_experts, gate_up_scales)
         w.down_experts = _lib.tensor(down_experts, down_scales)
@@ -56,6 +57,7 @@ class MoE:
         w.e_score_correction_bias = _lib.tensor(e_score_correction_bias)
         w.router_weight = _lib.tensor(router_weight)
         w.router_bias = _lib.tensor(router_bias)
+        w.shared_gate = _lib.tensor(shared_gate)
         _lib.check(_lib.lib().moe_set_weights(self._h, C.byref(w)))
         # the library borrows these buffers: keep them alive while bound
         self._bound = dict(gate_up_experts=gate_up_experts, down_experts=down_experts,
@@ -64,13 +66,13 @@ class MoE:
                            e_score_correction_bias=e_score_correction_bias,
                            gate_up_scales=gate_up_scales, down_scales=down_scales,
                            gate_scales=gate_scales, router_weight=router_weight,
-                           router_bias=router_bias)
+                           router_bias=router_bias, shared_gate=shared_gate)
 
     def set_weights_from(self, inp: dict):
         """Bind from a dict keyed by slot name (as ``synth.make_inputs`` returns)."""
         keys = ("gate_up_experts", "down_experts", "gate_experts", "gate_up_bias",
                 "down_bias", "gate_bias", "e_score_correction_bias", "gate_up_scales",
-                "down_scales", "gate_scales", "router_weight", "router_bias")
+                "down_scales", "gate_scales", "router_weight", "router_bias", "shared_gate")
         kw = {k: inp.get(k) for k in keys}
         self.set_weights(kw.pop("gate_up_experts"), kw.pop("down_experts"), **kw)
 

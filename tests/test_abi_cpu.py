@@ -127,6 +127,15 @@ def test_set_weights_validation(L):
     w.gate_up_experts = _t(L, [8, 64, 64], L.MOE_DTYPE_F32)   # dtype mismatch
     assert lib.moe_set_weights(h, C.byref(w)) == 2
     w.gate_up_experts = _t(L, [8, 64, 64], BF)
+    w.shared_gate = _t(L, [63], BF)                           # shared gate g must be [H]
+    assert lib.moe_set_weights(h, C.byref(w)) == 2
+    w.shared_gate = _t(L, [64], L.MOE_DTYPE_F32)              # ... in x's dtype
+    assert lib.moe_set_weights(h, C.byref(w)) == 2
+    w.shared_gate = _t(L, [64], BF)                           # binds whatever was declared
+    assert lib.moe_set_weights(h, C.byref(w)) == 0
+    mask = C.c_uint32()
+    assert lib.moe_borrowed_slots(h, C.byref(mask)) == 0
+    assert mask.value & L.SLOT_BITS["shared_gate"]
     w.gate_experts = _t(L, [8, 32, 64], BF)                   # unfused slot on fused layout
     assert lib.moe_set_weights(h, C.byref(w)) == 2
     lib.moe_destroy(h)

@@ -410,6 +410,29 @@ def test_shared_output_and_3d_input():
     compare_out(out.view(96, cfg.H), ref, "bf16", "shared + 3-D")
 
 
+@pytest.mark.parametrize("x_dtype,variant,weigh", [("bf16", 1, False), ("bf16", 2, False),
+                                                   ("bf16", 3, True), ("f32", 0, False)])
+def test_shared_gate(x_dtype, variant, weigh):
+    """logicaffeine "Moe" `shared_gate`: with a bound gate g [H] the shared
+    output enters scaled by sigmoid(x . g) (the route kernel's fp64 dot
+    product per token, the combine's scale); without a shared output the gate
+    is not read and the layer is the routed sum alone."""
+    w_dtype = "f32" if x_dtype == "f32" else "bf16"
+    cfg = synth.MoeConfig(name="sg", cid=217, T=300, H=256, I=128, E=8, K=2,
+                          x_dtype=x_dtype, w_dtype=w_dtype, shared_output=True,
+                          shared_gate=True, weigh_inputs=weigh)
+    inp = synth.make_inputs(cfg, device=DEV)
+    d = inp["x"].double().cpu() @ inp["shared_gate"].double().cpu()
+    assert (torch.sigmoid(d) < 0.2).any() and (torch.sigmoid(d) > 0.8).any()   # spread gates
+    out, r, _ = run_gpu(cfg, inp, gemm_variant=variant)
+    check_routing(cfg, inp, r, cfg.T)
+    compare_out(out, oracle_full(cfg, inp)["out"], x_dtype, f"shared gate {x_dtype} v{variant}")
+    # no shared output: the gate is ignored
+    inp2 = {k: v for k, v in inp.items() if k != "shared_output"}
+    out2, _, _ = run_gpu(cfg.replace(shared_output=False), inp2, gemm_variant=variant)
+    compare_out(out2, oracle_full(cfg, inp2)["out"], x_dtype, f"gate without shared {x_dtype}")
+
+
 def test_deterministic():
     """No value atomics: two runs give bitwise-identical outputs and routing."""
     cfg = synth.DEEPSEEK_SMALL
