@@ -182,7 +182,7 @@ typedef struct moe_tensor {
  *                    scaled by the logistic sigmoid of x . g).  When bound, a
  *                    forward given shared_output adds sigmoid(x[t] . g) *
  *                    shared_output[t] instead of shared_output[t] (x . g
- *                    accumulated in f32); without shared_output it is not
+ *                    accumulated in fp64); without shared_output it is not
  *                    read.  Binds whatever was declared. */
 typedef struct moe_weights {
     moe_tensor gate_up_experts;
@@ -291,7 +291,8 @@ moe_status moe_workspace_size(const moe_layer *layer, int64_t T, size_t *bytes);
  * logits are then x . Wr + Br, computed on the GPU (f32 accumulation).
  * x dtype: F32 for F32 weights, BF16 for BF16 or MXFP4 weights.  Optional
  * shared_output (the shared-expert branch, EXACTLY x's shape and dtype) is
- * added inside the combine.  `routing` (nullable) receives copies of the
+ * added inside the combine, scaled per token by sigmoid(x[t] . g) when the
+ * shared_gate slot is bound.  `routing` (nullable) receives copies of the
  * routing state.  T = 0 launches nothing.
  * Errors: INVALID_ARGUMENT, SHAPE_MISMATCH, UNBOUND, UNSUPPORTED, WORKSPACE,
  * HIP.  Concurrent calls on one layer are allowed with distinct workspaces. */
