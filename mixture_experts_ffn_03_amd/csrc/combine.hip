@@ -11,7 +11,8 @@
 // dtype (round to nearest even for bf16).  No atomics: each output element
 // is produced by one thread, so results are bitwise reproducible.  A chunk
 // of y the down GEMM stored in fp16 (its format byte says so) is read as
-// fp16 and widened exactly.
+// fp16 and widened exactly.  y is read once, with non-temporal loads
+// (DeepSeek-V3-shaped step: 0.203 -> 0.186 ms).
 #include "moe_kernels.h"
 
 namespace moe {
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
                 const int jj = p / S, sp = p % S;
                 const float *yr = a.y + sp * a.split_stride + (int64_t)row[jj] * a.H;
                 fmt[p] = a.yfmt[sp * a.yfmt_split_stride + (int64_t)row[jj] * a.yfmt_stride + q];
-                h[p] = *(const f16x8 *)((const _Float16 *)(yr + q0) + (c - q0));
+                h[p] = __builtin_nontemporal_load((const f16x8 *)((const _Float16 *)(yr + q0) + (c - q0)));
             }
         }
 #pragma unroll
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
                     for (int e = 0; e < 8; ++e) v[e] += (float)h[p][e];
                 } else {
                     const float *yr = a.y + sp * a.split_stride + (int64_t)row[jj] * a.H + c;
-                    const f32x4 lo = *(const f32x4 *)yr, hi = *(const f32x4 *)(yr + 4);
+                    const f32x4 lo = __builtin_nontemporal_load((const f32x4 *)yr), hi = __builtin_nontemporal_load((const f32x4 *)(yr + 4));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         v[e] += lo[e];
