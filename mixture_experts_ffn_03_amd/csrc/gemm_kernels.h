@@ -306,9 +306,18 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
         const uint16_t *bgp = g.w.b_gate ? (const uint16_t *)g.w.b_gate : g_zero_bias;
         const uint16_t *bup = (GATED && g.w.b_up) ? (const uint16_t *)g.w.b_up : g_zero_bias;
         const int64_t bgs = g.w.b_gate ? 1 : 0, bus = (GATED && g.w.b_up) ? 1 : 0;
-        auto pass1 = [&](auto bias_tag, auto act) {
+        // FAST: no biases, no row weights and every feature of this wave
+        // below Nout (the common case): no bias reads, no scaling and no
+        // per-value column test.  The max is kept per 32-row block and the
+        // rows past the tile's tokens (whose LDS rows were never loaded) are
+        // dropped once per block.  In a one-wave-per-SIMD tile every VALU
+        // instruction here costs the matrix pipe four idle cycles.
+        auto pass1 = [&](auto bias_tag, auto fast_tag, auto act) {
             constexpr bool BIAS = decltype(bias_tag)::value;
-            float hm = 0.0f;
+            constexpr bool FAST = decltype(fast_tag)::value;
+            float hmb[TL::FM];
+#pragma unroll
+            for (int m = 0; m < TL::FM; ++m) hmb[m] = 0.0f;
 #pragma unroll
             for (int fp = 0; fp < FH; ++fp)
 #pragma unroll
@@ -316,7 +325,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
                     const int c = tw.n0 + wn * WH + fp * 32 + i4 * 8 + fq;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const bool c_ok = c + j < g.Nout;
+                        const bool c_ok = FAST || c + j < g.Nout;
                         float bg = 0.0f, bu = 0.0f;
                         if constexpr (BIAS) {
                             const int64_t f = eb + (int64_t)min(c + j, g.Nout - 1) * g.w.row_mul;
@@ -325,24 +334,32 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
                         }
 #pragma unroll
                         for (int m = 0; m < TL::FM; ++m) {
-                            float gv = acc[fp][m][i4 * 4 + j] * rs[m];
+                            float gv = acc[fp][m][i4 * 4 + j];
+                            if constexpr (!FAST) gv *= rs[m];
                             if constexpr (BIAS) gv += bg;
                             float uv = 0.0f;
                             if constexpr (GATED) {
-                                uv = acc[fp + TL::FN / 2][m][i4 * 4 + j] * rs[m];
+                                uv = acc[fp + TL::FN / 2][m][i4 * 4 + j];
+                                if constexpr (!FAST) uv *= rs[m];
                                 if constexpr (BIAS) uv += bu;
                             }
                             const float h = act(gv, uv);
                             acc[fp][m][i4 * 4 + j] = h;
-                            hm = fmaxf(hm, (c_ok && tok_ok[m]) ? fabsf(h) : 0.0f);
+                            hmb[m] = fmaxf(hmb[m], c_ok ? fabsf(h) : 0.0f);
                         }
                     }
                 }
+            float hm = 0.0f;
+#pragma unroll
+            for (int m = 0; m < TL::FM; ++m) hm = fmaxf(hm, tok_ok[m] ? hmb[m] : 0.0f);
             return hm;
         };
         const bool bias = bgs != 0 || bus != 0;
+        const bool fast = !bias && !g.row_w && tw.n0 + (wn + 1) * WH <= g.Nout;
         auto run = [&](auto act) {
-            return bias ? pass1(std::true_type{}, act) : pass1(std::false_type{}, act);
+            if (fast) return pass1(std::false_type{}, std::true_type{}, act);
+            return bias ? pass1(std::true_type{}, std::false_type{}, act)
+                        : pass1(std::false_type{}, std::false_type{}, act);
         };
         float hmax;
         if constexpr (GATED) {
@@ -383,36 +400,53 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
         if constexpr (STAGED) {
             uint8_t *hs = lds + 256;
             __syncthreads();                 // every wave has read s_red
+            // one loop per storage format (the format test per value put a
+            // branch around every LDS write)
+            auto park = [&](auto f16_tag) {
+                constexpr bool H16 = decltype(f16_tag)::value;
 #pragma unroll
-            for (int fp = 0; fp < FH; ++fp)
+                for (int fp = 0; fp < FH; ++fp)
 #pragma unroll
-                for (int m = 0; m < TL::FM; ++m) {
-                    const int tl = wm * TL::TM + m * 32 + lrow;
+                    for (int m = 0; m < TL::FM; ++m) {
+                        const int tl = wm * TL::TM + m * 32 + lrow;
 #pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4) {
-                        const int cl = wn * WH + fp * 32 + i4 * 8 + fq;   // feature in tile
-                        const f32x16 &a = acc[fp][m];
-                        const int r0 = i4 * 4;
-                        uint8_t *dst = hs + tl * PITCH + cl * 2;
-                        if (f16) {
-                            f16x4 o = {(_Float16)a[r0], (_Float16)a[r0 + 1], (_Float16)a[r0 + 2],
-                                       (_Float16)a[r0 + 3]};
-                            *(f16x4 *)dst = o;
-                        } else {
-                            bf16x4 o = {(__bf16)a[r0], (__bf16)a[r0 + 1], (__bf16)a[r0 + 2],
-                                        (__bf16)a[r0 + 3]};
-                            *(bf16x4 *)dst = o;
+                        for (int i4 = 0; i4 < 4; ++i4) {
+                            const int cl = wn * WH + fp * 32 + i4 * 8 + fq;   // feature in tile
+                            const f32x16 &a = acc[fp][m];
+                            const int r0 = i4 * 4;
+                            uint8_t *dst = hs + tl * PITCH + cl * 2;
+                            if constexpr (H16) {
+                                f16x4 o = {(_Float16)a[r0], (_Float16)a[r0 + 1],
+                                           (_Float16)a[r0 + 2], (_Float16)a[r0 + 3]};
+                                *(f16x4 *)dst = o;
+                            } else {
+                                bf16x4 o = {(__bf16)a[r0], (__bf16)a[r0 + 1], (__bf16)a[r0 + 2],
+                                            (__bf16)a[r0 + 3]};
+                                *(bf16x4 *)dst = o;
+                            }
                         }
                     }
-                }
+            };
+            if (f16) park(std::true_type{});
+            else park(std::false_type{});
             __syncthreads();
+            // every chunk's LDS read goes out before the first store
             constexpr int CPRH = HW / 8;                     // 16-byte chunks per h row
-            for (int q = tid; q < TL::BM * CPRH; q += TL::NT) {
+            constexpr int NQ = (TL::BM * CPRH + TL::NT - 1) / TL::NT;
+            u32x4 hv[NQ];
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int q = tid + i * TL::NT;
+                if (q < TL::BM * CPRH)
+                    hv[i] = *(const u32x4 *)(hs + (q / CPRH) * PITCH + (q % CPRH) * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int q = tid + i * TL::NT;
                 const int r = q / CPRH, ch = q % CPRH;
                 const int c = tw.n0 + ch * 8;
-                if (r < tw.nrows && c < g.Nout)
-                    *(u32x4 *)(h + (int64_t)(tw.row0 + r) * g.Nout + c) =
-                        *(const u32x4 *)(hs + r * PITCH + ch * 16);
+                if (q < TL::BM * CPRH && r < tw.nrows && c < g.Nout)
+                    *(u32x4 *)(h + (int64_t)(tw.row0 + r) * g.Nout + c) = hv[i];
             }
         } else {
 #pragma unroll
