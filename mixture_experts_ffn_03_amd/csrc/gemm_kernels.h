@@ -306,9 +306,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
         const uint16_t *bgp = g.w.b_gate ? (const uint16_t *)g.w.b_gate : g_zero_bias;
         const uint16_t *bup = (GATED && g.w.b_up) ? (const uint16_t *)g.w.b_up : g_zero_bias;
         const int64_t bgs = g.w.b_gate ? 1 : 0, bus = (GATED && g.w.b_up) ? 1 : 0;
-        // FAST: no biases, no row weights and every feature of this wave
-        // below Nout (the common case): no bias reads, no scaling and no
-        // per-value column test.  The max is kept per 32-row block and the
+        // FAST: no row weights and every feature of this wave below Nout
+        // (the common case): no scaling and no per-value column test.  The max is kept per 32-row block and the
         // rows past the tile's tokens (whose LDS rows were never loaded) are
         // dropped once per block.  In a one-wave-per-SIMD tile every VALU
         // instruction here costs the matrix pipe four idle cycles.
@@ -355,9 +354,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
             return hm;
         };
         const bool bias = bgs != 0 || bus != 0;
-        const bool fast = !bias && !g.row_w && tw.n0 + (wn + 1) * WH <= g.Nout;
+        const bool fast = !g.row_w && tw.n0 + (wn + 1) * WH <= g.Nout;
         auto run = [&](auto act) {
-            if (fast) return pass1(std::false_type{}, std::true_type{}, act);
+            if (fast) {
+                return bias ? pass1(std::true_type{}, std::true_type{}, act)
+                            : pass1(std::false_type{}, std::true_type{}, act);
+            }
             return bias ? pass1(std::true_type{}, std::false_type{}, act)
                         : pass1(std::false_type{}, std::false_type{}, act);
         };
@@ -487,8 +489,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
             // store path for both: two made the 4-wave tile spill.)
             static_assert(TL::TN == kYWidth, "one y chunk per wave and row");
             const int q0 = tw.n0 + wn * TL::TN;
-            auto chunks = [&](auto with_bias) {
+            // FULL: the wave's whole chunk lies below Nout (no column tests)
+            auto chunks = [&](auto with_bias, auto full_tag) {
                 constexpr bool B = decltype(with_bias)::value;
+                constexpr bool FULL = decltype(full_tag)::value;
                 float bv[TL::FN][16];
                 if constexpr (B) {
 #pragma unroll
@@ -520,7 +524,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
 #pragma unroll
                         for (int i = 0; i < 16; ++i) {
                             v[f][i] = yval(f, m, i);
-                            if (q0 + f * 32 + (i / 4) * 8 + fq < g.Nout) mx = fmaxf(mx, fabsf(v[f][i]));
+                            if (FULL || q0 + f * 32 + (i / 4) * 8 + fq < g.Nout)
+                                mx = fmaxf(mx, fabsf(v[f][i]));
                         }
                     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
                     const int tl = wm * TL::TM + m * 32 + lrow;
@@ -536,7 +541,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
 #pragma unroll
                         for (int i4 = 0; i4 < 4; ++i4) {
                             const int cc = f * 32 + i4 * 8 + fq, r0 = i4 * 4;
-                            if (q0 + cc >= g.Nout) continue;
+                            if (!FULL && q0 + cc >= g.Nout) continue;
                             if (h16) {
                                 f16x4 o = {(_Float16)v[f][r0], (_Float16)v[f][r0 + 1],
                                            (_Float16)v[f][r0 + 2], (_Float16)v[f][r0 + 3]};
@@ -548,8 +553,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const TileWork &tw,
                         }
                 }
             };
-            if (bias) chunks(std::true_type{});
-            else chunks(std::false_type{});
+            const bool full = q0 + kYWidth <= g.Nout;
+            if (full) {
+                if (bias) chunks(std::true_type{}, std::true_type{});
+                else chunks(std::false_type{}, std::true_type{});
+            } else {
+                if (bias) chunks(std::true_type{}, std::false_type{});
+                else chunks(std::false_type{}, std::false_type{});
+            }
             return;
         }
         // plain (router logits [T, Nout], Nout = E of any size): a lane's 4
