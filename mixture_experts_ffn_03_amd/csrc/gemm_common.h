@@ -35,26 +35,37 @@ struct TileWork {
 // cut into 8 contiguous chunks, one per XCD (its L2 then serves the shared
 // panels and rows), and workgroup slot b / 8 walks its XCD's full chunk and
 // then its partial chunk.  The count of tiles is data dependent: the
-// prefix sums, and the experts' row counts and offsets, are staged in LDS
-// together (one round trip to memory; s_cum holds 4 (E + 1) ints), and
-// surplus workgroups of the worst-case grid return at once.
+// prefix sums, and the experts' row counts and offsets, are read with scalar
+// loads (the values are the same for every workgroup of the launch, so after
+// the first workgroup on a CU they come from the scalar cache instead of a
+// vector round trip to L2 at every tile start), and surplus workgroups of
+// the worst-case grid return at once.  s_cum is not used.
+//
+// Scalar loads of launch-constant ints, each statement waiting for its own
+// loads (no result register is left in flight).
+__device__ __forceinline__ int sload(const int *p)
+{
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+__device__ __forceinline__ void sload2(const int *p, const int *q, int &a, int &b)
+{
+    asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(a), "=&s"(b) : "s"(p), "s"(q) : "memory");
+}
+
 __device__ inline bool find_tile(const GemmArgs &g, int *s_cum, int n_width, TileWork *w)
 {
-    int *s_full = s_cum + g.E + 1;
-    int *s_cnt = s_full + g.E + 1;
-    int *s_off = s_cnt + g.E + 1;
-    for (int i = threadIdx.x; i <= g.E; i += blockDim.x) {
-        s_cum[i] = g.tile_cum[i];
-        s_full[i] = g.full_cum[i];
-        s_off[i] = g.offsets[i];
-        s_cnt[i] = i < g.E ? g.counts[i] : 0;
-    }
-    __syncthreads();
+    (void)s_cum;
+    const int E = g.E;
     // a split reduction multiplies the feature tiles: tile column
     // s * nN + nt is split s of feature tile nt
     const int nN = g.nN * g.ksplit;
-    const int F = s_full[g.E] * nN;               // full tiles
-    const int P = s_cum[g.E] * nN - F;            // partial tiles (one per expert and N tile)
+    int full_e, cum_e;
+    sload2(g.full_cum + E, g.tile_cum + E, full_e, cum_e);
+    const int F = full_e * nN;                    // full tiles
+    const int P = cum_e * nN - F;                 // partial tiles (one per expert and N tile)
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int qF = F >> 3, rF = F & 7, qP = P >> 3, rP = P & 7;
     const int cntF = qF + (xcd < rF ? 1 : 0);
@@ -62,41 +73,50 @@ __device__ inline bool find_tile(const GemmArgs &g, int *s_cum, int n_width, Til
     int e, nt, mtile;
     if (slot < cntF) {
         const int v = xcd * qF + min(xcd, rF) + slot;
-        // expert e with s_full[e]*nN <= v < s_full[e+1]*nN
-        int lo = 0, hi = g.E;
+        // expert e with full_cum[e]*nN <= v < full_cum[e+1]*nN
+        int lo = 0, hi = E;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (s_full[mid] * nN <= v) lo = mid;
+            if (sload(g.full_cum + mid) * nN <= v) lo = mid;
             else hi = mid;
         }
         e = lo;
-        const int mt = s_full[e + 1] - s_full[e];
-        const int local = v - s_full[e] * nN;
+        int f0, f1;
+        sload2(g.full_cum + e, g.full_cum + e + 1, f0, f1);
+        const int mt = f1 - f0;
+        const int local = v - f0 * nN;
         nt = local / mt;
         mtile = local - nt * mt;
     } else if (slot < cntF + cntP) {
         const int v = xcd * qP + min(xcd, rP) + (slot - cntF);
-        // partial tiles before expert e: (s_cum[e] - s_full[e]) * nN
-        int lo = 0, hi = g.E;
+        // partial tiles before expert e: (tile_cum[e] - full_cum[e]) * nN
+        int lo = 0, hi = E;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if ((s_cum[mid] - s_full[mid]) * nN <= v) lo = mid;
+            int c, f;
+            sload2(g.tile_cum + mid, g.full_cum + mid, c, f);
+            if ((c - f) * nN <= v) lo = mid;
             else hi = mid;
         }
         e = lo;
-        nt = v - (s_cum[e] - s_full[e]) * nN;
+        int c0, f0;
+        sload2(g.tile_cum + e, g.full_cum + e, c0, f0);
+        nt = v - (c0 - f0) * nN;
         mtile = 0;                                // the expert's only tile
     } else {
         return false;
     }
+    int c0, c1, cnt, off;
+    sload2(g.tile_cum + e, g.tile_cum + e + 1, c0, c1);
+    sload2(g.counts + e, g.offsets + e, cnt, off);
     // rows of M-tile mtile of the expert's ntl tiles
-    const int ntl = s_cum[e + 1] - s_cum[e], cnt = s_cnt[e];
+    const int ntl = c1 - c0;
     const int r0 = (int)((int64_t)mtile * cnt / ntl);
     const int r1 = (int)((int64_t)(mtile + 1) * cnt / ntl);
     w->e = e;
-    w->row0 = s_off[e] + r0;
+    w->row0 = off + r0;
     w->nrows = r1 - r0;
-    w->mg = s_cum[e] + mtile;
+    w->mg = c0 + mtile;
     w->ks = nt / g.nN;
     nt -= w->ks * g.nN;
     w->n0 = nt * n_width;
