@@ -759,6 +759,15 @@ __device__ __forceinline__ void dma16_w(const void *src, uint32_t lds_byte)
     else dma16(src, lds_byte);
 }
 
+// The same load in the scalar-base form: the address is a uniform 64-bit
+// base in SGPRs plus this lane's 32-bit offset, so a k-step moves only the
+// base (one scalar add for all of a thread's loads) and the loads need no
+// per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_t lds_byte)
+{
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_byte) : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_offset(const void *p)
 {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
@@ -819,6 +828,8 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
     const uint8_t *b_src[TL::NBC];
     int b_k[TL::NBC];
     const uint8_t *s_src = nullptr;
+    const uint8_t *b_blk = nullptr;      // the tile's block of the prepared copy
+    uint32_t b_off[TL::NBC] = {};         // this load's byte offset in a block
     if constexpr (TL::MX) {
         // logical row-block (packed layout) of tile row-block t
         const int nrb_tot = (GATED ? 2 : 1) * g.nrb_half;
@@ -846,6 +857,7 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
         constexpr int SUB = kPack16Rows / TL::BN;               // tiles per block
         const int bi = tw.nt / SUB, h = tw.nt % SUB;
         const uint8_t *blk = g.wpk + ((int64_t)tw.e * g.nks * pk_nblk + bi) * kPack16Stage;
+        b_blk = blk;
 #pragma unroll
         for (int i = 0; i < TL::NBC; ++i) {
             const int q = (i * TL::NWAVES + wave) * 64 + lane;
@@ -855,7 +867,8 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
                                                          (r - TL::BN / 2))
                                  : h * TL::BN + r;
             b_k[i] = 0;
-            b_src[i] = blk + (pr * TL::CPR + q % TL::CPR) * 16;
+            b_off[i] = (uint32_t)((pr * TL::CPR + q % TL::CPR) * 16);
+            b_src[i] = blk + b_off[i];
         }
     } else {
 #pragma unroll
@@ -958,10 +971,12 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
                 dma16_w<TL, EPI>(s_src + (int64_t)kc * 64, wave_sc + (kt % TL::SB) * TL::B_BYTES);
             }
         } else {
+            // the 16-bit interleaved loop streams the prepared copy only (the
+            // launchers send a layer without one to the 8-wave tile): a
+            // uniform block base per k-step and fixed lane offsets, and no
+            // ragged select (the copy is zero past the reduction length)
             const uint32_t st = wave_lds + TL::B_BASE + (kt % TL::SB) * TL::B_BYTES;
-            const uint8_t *p = b_src[i] + (uint64_t)kc * b_step;
-            if (RAGGED && b_ragged) p = ((int)kc * TL::BK + b_k[i] < Kd) ? p : zero;
-            dma16_w<TL, EPI>(p, st + i * TL::NWAVES * 1024);
+            dma16s(b_off[i], b_blk + (uint64_t)kc * b_step, st + i * TL::NWAVES * 1024);
         }
     };
     auto issue_a = [&](int kt) {
