@@ -975,6 +975,7 @@ moe_status moe::forward_impl(const moe_layer *l, const moe_tensor *x, const moe_
     // GEMM 1: gate||up with the fused activation -> h
     GemmArgs g1{};
     g1.a = x->data;
+    g1.a_off32 = T * l->H * (x->dtype == MOE_DTYPE_F32 ? 4 : 2) <= (int64_t(1) << 32) ? 1 : 0;
     g1.row_token = (const int32_t *)(wsb + W.row_token);
     g1.counts = (const int32_t *)(wsb + W.counts);
     g1.offsets = (const int32_t *)(wsb + W.offsets);
@@ -1004,6 +1005,7 @@ moe_status moe::forward_impl(const moe_layer *l, const moe_tensor *x, const moe_
     // GEMM 2: down + bias -> y (f32 space; in-range chunks stored in fp16 when yfmt is set)
     GemmArgs g2{};
     g2.a = wsb + W.h;
+    g2.a_off32 = T * l->K * l->I * 2 <= (int64_t(1) << 32) ? 1 : 0;
     g2.row_token = nullptr;
     g2.counts = g1.counts;
     g2.offsets = g1.offsets;

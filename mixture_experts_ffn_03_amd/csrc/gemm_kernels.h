@@ -953,9 +953,24 @@ __device__ __forceinline__ void dma_body(const GemmArgs &g, const TileWork &tw, 
         a_base[i] = a_ok[i] ? a_src[i] : zero;
         a_step[i] = a_ok[i] ? 2 * TL::BK : 0;
     }
+    // The 4-wave 16-bit tile with a whole number of k-steps: token chunk i of
+    // a k-step is a + k-step offset (uniform, in SGPRs) + a fixed 32-bit lane
+    // offset (the launcher checks that A lies within 4 GiB).  A row past the
+    // tile's tokens reads its clamped row's data (finite values in rows whose
+    // outputs are dropped) instead of the zero chunk.
+    constexpr bool A_SBASE = !TL::MX && TL::WPE == 1 && !RAGGED;
+    uint32_t a_voff[TL::NA];
+#pragma unroll
+    for (int i = 0; i < TL::NA; ++i)
+        a_voff[i] = (uint32_t)(a_src[i] - (const uint8_t *)g.a);
     auto issue_a_nb = [&](int kt, int i) {
         const uint32_t st = wave_lds + (kt % TL::SA) * TL::A_BYTES;
         const uint32_t kc = (uint32_t)(kbeg + min(kt, nk - 1));
+        if constexpr (A_SBASE) {
+            dma16s(a_voff[i], (const uint8_t *)g.a + (uint64_t)kc * (2 * TL::BK),
+                   st + i * TL::NWAVES * 1024);
+            return;
+        }
         const uint8_t *p = a_base[i] + (uint64_t)kc * a_step[i];
         if (RAGGED) p = ((int)kc * TL::BK + a_k[i] < Kd) ? p : zero;
         dma16(p, st + i * TL::NWAVES * 1024);

@@ -129,6 +129,9 @@ struct GemmArgs {
     int nks;                     // k-steps of 64 (the reduction length, rounded
                                  // up): MXFP4 and prepared 16-bit copies
     int nrb_half;                // row-blocks of one operand (Nout / 32)
+    int a_off32;                 // every byte of the A operand lies within 4 GiB
+                                 // of a (the 4-wave 16-bit tile addresses its
+                                 // token rows as a + 32-bit lane offsets)
 };
 
 // Prepare-time repack of an MXFP4 weight stack into the layout the GEMM
