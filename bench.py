@@ -223,9 +223,23 @@ class Workload:
             d["gemms_weight_stream_gbs"] = self.stream_bytes() / (d["gemm_ms"] * 1e-3) / 1e9
             d["gemms_hbm_frac"] = d["gemms_weight_stream_gbs"] / PEAK_HBM_GBS
         else:
-            roof = {"bound": "mfma", "kernel": "gate||up grouped GEMM",
-                    "achieved": gemm1_flops / (g1 * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s"}
+            # the bound is whichever floor is the longer: the MFMA work at the
+            # dense bf16 peak, or the touched weights plus x and h at HBM peak
+            # (the skewed DeepSeek-V3 shape streams 13 GB of gate||up weights)
+            g1_bytes = (self.touched * self.gu_bytes + cfg.T * cfg.H * 2
+                        + cfg.T * cfg.K * cfg.I * 2)
+            floor_mfma = gemm1_flops / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+            floor_hbm = g1_bytes / (PEAK_HBM_GBS * 1e9) * 1e3
+            if floor_hbm > floor_mfma:
+                roof = {"bound": "hbm", "kernel": "gate||up grouped GEMM",
+                        "achieved": g1_bytes / (g1 * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s"}
+            else:
+                roof = {"bound": "mfma", "kernel": "gate||up grouped GEMM",
+                        "achieved": gemm1_flops / (g1 * 1e-3) / 1e12,
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+            roof["floors_ms"] = {"mfma": round(floor_mfma, 4), "hbm": round(floor_hbm, 4)}
+            roof["mfma_frac"] = gemm1_flops / (g1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
             gemm2_flops = 2.0 * cfg.T * cfg.K * cfg.H * cfg.I
             d["gemm_down_frac"] = gemm2_flops / (stage_ms["gemm_down"] * 1e-3) / 1e12 \
                 / PEAK_BF16_TFLOPS
