@@ -768,10 +768,10 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_
     asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_byte) : "memory");
 }
 
-// The same with the non-temporal cache policy: the gate||up short body's
-// weights (a tile of at most 128 rows is, but for a rare row count, the one
-// tile of a small expert, so no other tile reads its weight panel; DeepSeek-
-// V3-shaped gate||up 4.38 -> 4.32 ms.  In the down GEMM it measured no gain).
+// The same with the non-temporal cache policy, for the weights of the
+// gate||up short body.  A tile of at most 128 rows is almost always the only
+// tile of a small expert, so no other tile reads its weight panel (DeepSeek-
+// V3-shaped gate||up 4.38 -> 4.32 ms; in the down GEMM it measured no gain).
 __device__ __forceinline__ void dma16s_nt(uint32_t voff, const void *sbase, uint32_t lds_byte)
 {
     asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds_byte) : "memory");
