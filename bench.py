@@ -14,6 +14,8 @@ it carries:
     the weight-stream rate (touched experts' weight bytes per step);
   - "workloads": the gpt-oss-20b-shaped MXFP4 layer and the DeepSeek-V3-shaped
     layer (and the decode step again), each with its own roofline object.
+  - "decode.graph_replay": the same decode step captured once into a HIP graph
+    and replayed (no host launch gaps between its kernels), timed the same way.
 Each of these is timed step by step with HIP events on the launch stream
 (the step time from plain steps between two events, the stage times from a
 second pass with the library's stage events),
@@ -292,6 +294,41 @@ def timed_flushed(wl, hip, steps: int, warmup: int, scratch):
     return sum(plain) / len(plain), st, min(plain), sum(staged) / len(staged)
 
 
+def timed_graph(wl, steps: int, scratch):
+    """The step captured once into a HIP graph and replayed: a prepared
+    layer's forward on a caller workspace and output is kernel launches only,
+    so torch.cuda.graph can capture it (as a serving loop would) and a replay
+    drops the host launch gaps between the step's kernels.  Each replay is
+    timed between two events after the same 1 GiB scratch read as the eager
+    steps.  Returns (mean ms, min ms)."""
+    import torch
+    words = scratch.view(torch.int32)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        wl.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wl.step()
+    torch.cuda.synchronize()
+    words.max()
+    g.replay()
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for k in range(steps):
+        words.max()
+        pairs[k][0].record()
+        g.replay()
+        pairs[k][1].record()
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in pairs]
+    del g
+    return sum(t) / len(t), min(t)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -424,6 +461,11 @@ def main():
             d = sw.summary(s_ms, s_st, flushed=True)
             d["min_ms"] = s_min
             d["ms_per_step_with_stage_events"] = s_staged
+            if sw.decode:
+                g_ms, g_min = timed_graph(sw, args.sub_steps, scratch)
+                d["graph_ms_per_step"] = g_ms
+                d["graph_min_ms"] = g_min
+                d["graph_weight_stream_gbs"] = sw.stream_bytes() / (g_ms * 1e-3) / 1e9
             log(f"[bench] {name}: {s_ms:.4f} ms/step (flushed), gate||up "
                 f"{d['roofline']['frac']:.3f} of {d['roofline']['bound']} peak")
             subs[name] = d
@@ -441,6 +483,11 @@ def main():
                 "gemms_hbm_frac": q["gemms_hbm_frac"],
                 "ms_per_step": q["ms_per_step"], "mall_flushed_between_steps": True,
                 "roofline": q["roofline"]}
+            if "graph_ms_per_step" in q:
+                res["decode"]["graph_replay"] = {
+                    "ms_per_step": q["graph_ms_per_step"], "min_ms": q["graph_min_ms"],
+                    "weight_stream_gbs": q["graph_weight_stream_gbs"],
+                    "hbm_frac_step": q["graph_weight_stream_gbs"] / PEAK_HBM_GBS}
     print(json.dumps(res), flush=True)
 
 

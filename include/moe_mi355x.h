@@ -295,7 +295,12 @@ moe_status moe_workspace_size(const moe_layer *layer, int64_t T, size_t *bytes);
  * shared_gate slot is bound.  `routing` (nullable) receives copies of the
  * routing state.  T = 0 launches nothing.
  * Errors: INVALID_ARGUMENT, SHAPE_MISMATCH, UNBOUND, UNSUPPORTED, WORKSPACE,
- * HIP.  Concurrent calls on one layer are allowed with distinct workspaces. */
+ * HIP.  Concurrent calls on one layer are allowed with distinct workspaces.
+ * Once the layer is prepared (moe_prepare, or one earlier forward), a call
+ * enqueues kernel launches on `stream` only (plus device-to-device copies
+ * when `routing` is given): no allocation, memset or host synchronisation,
+ * so it may be captured into a HIP graph and replayed, with the captured
+ * buffers' contents changed between replays. */
 moe_status moe_forward(const moe_layer *layer, const moe_tensor *x,
                        const moe_tensor *router_logits,
                        const moe_tensor *shared_output, moe_tensor *out,
